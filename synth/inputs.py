@@ -1,0 +1,165 @@
+"""Seeded synthetic inputs for the MoGE layer (shared by the oracle tests, the
+GPU tests and the benchmark).
+
+This module draws random numbers and stores them in the layer's dtype.  It holds
+none of the layer's arithmetic: no routing, no softmax, no matmul.
+
+Recipe (every tensor):
+  * values are float32 draws of standard_normal * std from numpy's PCG64;
+  * a tensor is cut into chunks of CHUNK consecutive elements (row-major); chunk c
+    of tensor `tid` is drawn from SeedSequence([seed, tid, c]), so the values do
+    not depend on how many threads fill them;
+  * bf16 tensors are rounded from those float32 values to nearest-even and kept
+    as uint16 bit patterns (the upper half of the float32 word).
+
+Tensor ids: 0 x[T,d], 1 w_router[N,d], 2 w_gate[N,I,d], 3 w_up[N,I,d],
+4 w_down[N,d,I], 5 ws_gate[I_s,d], 6 ws_up[I_s,d], 7 ws_down[d,I_s],
+8 router scores for the routing-only calls [T,N] (std 1).
+
+Layouts are row-major with the contraction dimension contiguous for every weight:
+a gate/up row is one intermediate unit's d inputs, a down row is one output
+channel's I inputs.  The shared experts are stored concatenated along the
+intermediate dimension: shared expert s owns rows [s*shared_inter,
+(s+1)*shared_inter) of ws_gate/ws_up and the same columns of ws_down.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from .configs import LayerConfig
+
+CHUNK = 1 << 20
+
+TID_X, TID_WR, TID_WG, TID_WU, TID_WD, TID_WSG, TID_WSU, TID_WSD, TID_SCORES = range(9)
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen uint16 bf16 bit patterns to float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_tensor(shape, std: float, seed: int, tid: int, dtype: str) -> np.ndarray:
+    """Draw a tensor of N(0, std) values with the chunked recipe above.
+
+    dtype "f32" returns float32, "bf16" returns uint16 bit patterns."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    nchunks = (n + CHUNK - 1) // CHUNK
+    s32 = np.float32(std)
+
+    def fill(c: int) -> None:
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, c])))
+        v = g.standard_normal(hi - lo, dtype=np.float32)
+        v *= s32
+        if dtype == "bf16":
+            out[lo:hi] = f32_to_bf16_bits(v)
+        else:
+            out[lo:hi] = v
+
+    if nchunks <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(max_workers=_threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+def zipf_bias(N: int, s: float) -> np.ndarray:
+    """Per-expert router bias -s*ln(rank) with rank = e+1 (float32).
+
+    Adding it to the router scores makes the scores of expert e follow a
+    Zipf(s)-shaped preference: low-numbered experts are favoured, so a plain global
+    top-K overloads the first groups."""
+    return (-np.float32(s) * np.log(np.arange(1, N + 1, dtype=np.float64))).astype(np.float32)
+
+
+@dataclass
+class LayerInputs:
+    cfg: LayerConfig
+    x: np.ndarray                 # [T,d]
+    w_router: np.ndarray          # [N,d]
+    router_bias: Optional[np.ndarray]  # [N] float32 or None
+    w_gate: np.ndarray            # [N,I,d]
+    w_up: np.ndarray              # [N,I,d]
+    w_down: np.ndarray            # [N,d,I]
+    ws_gate: np.ndarray           # [I_s,d]
+    ws_up: np.ndarray             # [I_s,d]
+    ws_down: np.ndarray           # [d,I_s]
+
+    @property
+    def is_bf16(self) -> bool:
+        return self.cfg.dtype == "bf16"
+
+
+def make_layer_inputs(cfg: LayerConfig, T: Optional[int] = None,
+                      seed: Optional[int] = None) -> LayerInputs:
+    """All tensors of one layer call, seeded.  T overrides cfg.T (the weights do
+    not depend on T; x's first rows do not either, since x is drawn row-major)."""
+    T = cfg.T if T is None else T
+    seed = cfg.seed if seed is None else seed
+    dt = cfg.dtype
+    d, N, I, Is = cfg.d, cfg.N, cfg.inter, cfg.I_s
+    bias = zipf_bias(N, cfg.zipf_s) if cfg.zipf_s > 0 else None
+    return LayerInputs(
+        cfg=cfg,
+        x=normal_tensor((T, d), cfg.x_std, seed, TID_X, dt),
+        w_router=normal_tensor((N, d), cfg.router_std, seed, TID_WR, dt),
+        router_bias=bias,
+        w_gate=normal_tensor((N, I, d), cfg.w_std, seed, TID_WG, dt),
+        w_up=normal_tensor((N, I, d), cfg.w_std, seed, TID_WU, dt),
+        w_down=normal_tensor((N, d, I), cfg.w_std, seed, TID_WD, dt),
+        ws_gate=normal_tensor((Is, d), cfg.w_std, seed, TID_WSG, dt),
+        ws_up=normal_tensor((Is, d), cfg.w_std, seed, TID_WSU, dt),
+        ws_down=normal_tensor((d, Is), cfg.w_std, seed, TID_WSD, dt),
+    )
+
+
+def make_scores(cfg: LayerConfig, T: Optional[int] = None, seed: Optional[int] = None,
+                with_bias: bool = True) -> np.ndarray:
+    """Router scores [T,N] float32 ~ N(0,1) for the routing-only calls, plus the
+    Zipf bias when the workload has one.  These set the per-expert row counts of
+    the routing/permutation workloads."""
+    T = cfg.T if T is None else T
+    seed = cfg.seed if seed is None else seed
+    s = normal_tensor((T, cfg.N), 1.0, seed, TID_SCORES, "f32")
+    if with_bias and cfg.zipf_s > 0:
+        s = (s + zipf_bias(cfg.N, cfg.zipf_s)[None, :]).astype(np.float32)
+    return s
+
+
+def tie_scores(T: int, N: int, seed: int, levels: int = 3) -> np.ndarray:
+    """Scores with many exact ties (small integers, with +0.0 and -0.0 both
+    present) for the tie-breaking cases."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 99])))
+    v = g.integers(-levels, levels + 1, size=(T, N)).astype(np.float32)
+    neg0 = g.random((T, N)) < 0.5
+    v[(v == 0) & neg0] = np.float32(-0.0)
+    return v
+
+
+def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
+    """A sorted seeded sample of n distinct token indices (all tokens if n >= T);
+    always includes the first and last token."""
+    if n >= T:
+        return np.arange(T)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 77])))
+    pick = g.choice(np.arange(1, T - 1), size=max(0, n - 2), replace=False)
+    return np.unique(np.concatenate([[0, T - 1], pick])).astype(np.int64)
