@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Throughput of the MoGE expert-layer forward pass on one MI355X.
+
+One step = one moge_layer_forward call over one batch: router scores, global
+softmax, per-group top-K', permutation, routed SwiGLU experts, shared experts and
+the gate-weighted combine.  Inputs are seeded synthetic tensors already resident
+in HBM when the timed region starts.
+
+Prints ONE JSON line (the default workload is the decode batch of 64 tokens on
+the Pangu-Pro-shaped layer: d=5120, 64 experts in 8 groups, 1 per group, 4 shared
+experts, SwiGLU width 1344, bf16).  The line carries
+  * value: layer tokens/s over the K timed steps (wall clock around them);
+  * roofline: for the dominant kernel (gate/up + SwiGLU of routed and shared
+    experts), its algorithmic bytes (HBM-bound workloads) or flops (MFMA-bound
+    ones) per launch over its mean launch time, from HIP events the library
+    records on its own stream around that launch in every timed step;
+  * cpu_baseline: the CPU oracle timed on the host on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C1]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoGE layer tokens/s at 1 GPU; decode HBM GB/s % peak, prefill MFMA % peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+FFN_SOURCES = [os.path.join(ROOT, "sparse_moe_layer_moge_amd", "csrc", f)
+               for f in ("ffn.hip", "moge_common.hpp")]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="C1", help="workload: C0..C4 (default C1)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens in the CPU oracle sample (default: the whole batch, max 64)")
+    return ap.parse_args()
+
+
+def ffn_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in FFN_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Hip:
+    """hipEvent_t handles from the HIP runtime the process already uses."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.rt.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        assert self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e: int) -> None:
+        self.rt.hipEventDestroy(e)
+
+
+def algorithmic_work(cfg, counts):
+    """Bytes and flops the method itself needs (intermediates not counted).
+
+    Expert weights are counted once for every expert that receives at least one
+    row, plus the shared and router weights, x in and y out.  Flops count the
+    router, routed and shared matmuls (2 per multiply-add)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    d, I, Is, T, N = cfg.d, cfg.inter, cfg.I_s, cfg.T, cfg.N
+    R = T * cfg.K
+    active = int((counts > 0).sum())
+    gate_up = dict(bytes=active * 2 * d * I * es + 2 * d * Is * es + T * d * es + (R * I + T * Is) * es,
+                   flops=4 * R * d * I + 4 * T * d * Is)
+    down = dict(bytes=active * d * I * es + d * Is * es + (R * I + T * Is) * es + (R + T) * d * es,
+                flops=2 * R * d * I + 2 * T * d * Is)
+    layer = dict(bytes=active * 3 * d * I * es + 3 * d * Is * es + N * d * es + 2 * T * d * es,
+                 flops=2 * T * d * N + 6 * R * d * I + 6 * T * d * Is)
+    return dict(gate_up=gate_up, down=down, layer=layer, active_experts=active)
+
+
+def cpu_baseline(cfg, inp, n_tokens: int):
+    """Time the CPU oracle (numpy float64) on the first n_tokens tokens' outputs."""
+    import numpy as np
+    from oracle import moge_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    tok = np.arange(min(n_tokens, cfg.T))
+    t0 = time.perf_counter()
+    O.layer(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down,
+            inp.ws_gate, inp.ws_up, inp.ws_down, M=cfg.M, kp=cfg.kp, dtype=cfg.dtype,
+            tokens=tok)
+    dt = time.perf_counter() - t0
+    return {"value": len(tok) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(tok)} of the batch's {cfg.T} tokens through the whole layer "
+                      f"(routing over all {cfg.T} tokens), numpy float64, {dt:.1f} s"}
+
+
+def main() -> int:
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs the MoGE layer on one GPU only; "
+                                   f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported. "
+                                   "A multi-GPU layer would place one expert group per GPU "
+                                   "(all-gather of x, reduce-scatter of the outputs)."}))
+        return 2
+
+    import numpy as np
+    import torch
+    import sparse_moe_layer_moge_amd as moge
+    from synth import inputs as S
+    from synth.configs import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    t_setup = time.perf_counter()
+    inp = S.make_layer_inputs(cfg)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    x = dev(inp.x)
+    w = {k: dev(getattr(inp, k)) for k in ("w_router", "router_bias", "w_gate", "w_up", "w_down",
+                                           "ws_gate", "ws_up", "ws_down")}
+    dims = moge.make_dims(cfg.T, cfg.d, cfg.N, cfg.M, cfg.kp, cfg.inter, cfg.I_s,
+                          moge.MOGE_BF16 if cfg.dtype == "bf16" else moge.MOGE_F32)
+    ws = torch.empty(moge.workspace_size(dims), dtype=torch.uint8, device="cuda")
+    y = torch.empty((cfg.T, cfg.d), dtype=tdt, device="cuda")
+    idx = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda")
+    gc = torch.empty((cfg.M,), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def step():
+        moge.layer_forward(dims, x, w["w_router"], w["router_bias"], w["w_gate"], w["w_up"],
+                           w["w_down"], w["ws_gate"], w["ws_up"], w["ws_down"], y, ws,
+                           topk_idx_out=idx, group_counts_out=gc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    K = args.steps
+    evs = [[hip.event() for _ in range(moge.STAGE_EVENTS)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        moge.set_stage_events(evs[i])
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    moge.set_stage_events(None)
+
+    stage_ms = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(moge.STAGE_EVENTS - 1)]
+                         for e in evs])
+    for e in evs:
+        for h in e:
+            hip.destroy(h)
+    mean_stage = stage_ms.mean(axis=0)
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=cfg.N)
+    gcounts = gc.cpu().numpy()
+    work = algorithmic_work(cfg, counts)
+
+    ms_per_step = 1e3 * elapsed / K
+    value = cfg.T * K / elapsed
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    intensity = work["layer"]["flops"] / work["layer"]["bytes"]
+    bound = "mfma" if intensity > ridge else "hbm"
+    t_gu = mean_stage[3] * 1e-3
+    if bound == "hbm":
+        achieved = work["gate_up"]["bytes"] / t_gu / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = work["gate_up"]["flops"] / t_gu / 1e12
+        peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        unit = "TFLOP/s"
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f).get(f"gate_up@{cfg.name}")
+        if tr and tr.get("source_hash") == ffn_source_hash():
+            traffic = tr["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic (seeded N(0,std) inputs, random-init weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "N": cfg.N, "M": cfg.M,
+                   "k_per_group": cfg.kp, "inter": cfg.inter, "shared_experts": cfg.n_shared,
+                   "shared_inter_total": cfg.I_s, "parallelism": "single GPU"},
+        "roofline": {"bound": bound, "kernel": "gate_up+SwiGLU (routed+shared)",
+                     "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "algorithmic_bytes": work["gate_up"]["bytes"],
+                     "algorithmic_flops": work["gate_up"]["flops"],
+                     "mean_launch_ms": round(float(mean_stage[3]), 4)},
+        "stages_ms": {n: round(float(v), 4) for n, v in zip(moge.STAGE_NAMES, mean_stage)},
+        "layer": {"algorithmic_bytes": work["layer"]["bytes"],
+                  "algorithmic_flops": work["layer"]["flops"],
+                  "hbm_GBps": round(work["layer"]["bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+                  "tflops": round(work["layer"]["flops"] / (ms_per_step * 1e-3) / 1e12, 2),
+                  "active_experts": work["active_experts"],
+                  "rows_per_expert_min_max": [int(counts.min()), int(counts.max())],
+                  "imbalance_score": float(gcounts.max() - gcounts.min()) / cfg.T},
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_tokens if args.cpu_tokens > 0 else min(cfg.T, 64)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, n)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

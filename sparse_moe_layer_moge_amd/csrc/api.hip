@@ -1,0 +1,375 @@
+// C ABI of the MoGE layer library: host-side validation, workspace carving and
+// kernel dispatch on the caller's stream.  No device allocation, no host
+// synchronisation, no host reads of device data.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/moge.h"
+#include "moge_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_stage_events[MOGE_STAGE_EVENTS];
+thread_local bool g_record_stages = false;
+
+void mark(int i, hipStream_t st) {
+  if (g_record_stages) (void)hipEventRecord(g_stage_events[i], st);
+}
+
+moge_status_t fail(moge_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moge_status_t fail(moge_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moge_status_t ok() {
+  g_last_error.clear();
+  return MOGE_OK;
+}
+
+moge_status_t hip_check(hipError_t e, const char* where) {
+  if (e != hipSuccess)
+    return fail(MOGE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+  return MOGE_OK;
+}
+
+constexpr int kMaxExperts = 256;
+constexpr int kMaxSlots = 64;
+
+int esize(const moge_dims_t* d) { return d->dtype == MOGE_BF16 ? 2 : 4; }
+
+moge_status_t check_dims(const moge_dims_t* d) {
+  if (!d) return fail(MOGE_ERR_INVALID_ARG, "dims is NULL");
+  if (d->T < 0 || d->d <= 0 || d->N <= 0 || d->M <= 0 || d->k_per_group <= 0 || d->inter <= 0 ||
+      d->shared_inter < 0)
+    return fail(MOGE_ERR_INVALID_ARG,
+                "dims out of range (T=%d d=%d N=%d M=%d k_per_group=%d inter=%d shared_inter=%d)",
+                d->T, d->d, d->N, d->M, d->k_per_group, d->inter, d->shared_inter);
+  if (d->N % d->M != 0)
+    return fail(MOGE_ERR_INVALID_ARG, "N=%d is not a multiple of M=%d", d->N, d->M);
+  if (d->k_per_group > d->N / d->M)
+    return fail(MOGE_ERR_INVALID_ARG, "k_per_group=%d exceeds the group size N/M=%d",
+                d->k_per_group, d->N / d->M);
+  if (d->dtype != MOGE_F32 && d->dtype != MOGE_BF16)
+    return fail(MOGE_ERR_INVALID_ARG, "dtype=%d is not MOGE_F32 or MOGE_BF16", d->dtype);
+  if (d->N > kMaxExperts) return fail(MOGE_ERR_UNSUPPORTED, "N=%d > %d", d->N, kMaxExperts);
+  const int K = d->M * d->k_per_group;
+  if (K > kMaxSlots) return fail(MOGE_ERR_UNSUPPORTED, "K=M*k_per_group=%d > %d", K, kMaxSlots);
+  if (d->d % 32 || d->inter % 32 || d->shared_inter % 32)
+    return fail(MOGE_ERR_UNSUPPORTED, "d=%d, inter=%d and shared_inter=%d must be multiples of 32",
+                d->d, d->inter, d->shared_inter);
+  if ((long long)d->T * K >= (1ll << 31))
+    return fail(MOGE_ERR_UNSUPPORTED, "T*K=%lld rows exceed int32", (long long)d->T * K);
+  return MOGE_OK;
+}
+
+moge_status_t check_ptr(const void* p, size_t align, const char* name, bool required) {
+  if (!p) {
+    if (required) return fail(MOGE_ERR_INVALID_ARG, "%s is NULL", name);
+    return MOGE_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(p) % align)
+    return fail(MOGE_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return MOGE_OK;
+}
+
+#define CHECK(expr)                         \
+  do {                                      \
+    const moge_status_t s_ = (expr);        \
+    if (s_ != MOGE_OK) return s_;           \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// workspace layout (256-byte aligned regions)
+// ---------------------------------------------------------------------------
+struct Plan {
+  size_t partial, idx, gate, blk_cnt, blk_base, counts, offsets, gcounts, sorted_pair, pair_row,
+      h, hs, y_perm, sh, total;
+  int ksplit;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+Plan make_plan(const moge_dims_t* d) {
+  Plan p{};
+  const size_t T = d->T, N = d->N, M = d->M, K = (size_t)d->M * d->k_per_group, R = T * K;
+  const size_t es = esize(d), nblk = moge::perm_blocks(d->T);
+  p.ksplit = moge::router_ksplit(d->T, d->d, d->N);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes > 0 ? bytes : 1);
+    return at;
+  };
+  p.partial = take((size_t)p.ksplit * T * N * 4);
+  p.idx = take(T * K * 4);
+  p.gate = take(T * K * 4);
+  p.blk_cnt = take(nblk * N * 4);
+  p.blk_base = take(nblk * N * 4);
+  p.counts = take(N * 4);
+  p.offsets = take((N + 1) * 4);
+  p.gcounts = take(M * 4);
+  p.sorted_pair = take(R * 4);
+  p.pair_row = take(R * 4);
+  p.h = take(R * (size_t)d->inter * es);
+  p.hs = take(T * (size_t)d->shared_inter * es);
+  p.y_perm = take(R * (size_t)d->d * es);
+  p.sh = take(T * (size_t)d->d * es);
+  p.total = o;
+  return p;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+moge_status_t check_ws(const moge_dims_t* d, void* ws, size_t ws_bytes, Plan* plan) {
+  *plan = make_plan(d);
+  if (!ws) return fail(MOGE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", plan->total);
+  if (reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(MOGE_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (ws_bytes < plan->total)
+    return fail(MOGE_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, plan->total);
+  return MOGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moge_abi_version(void) { return 1; }
+
+moge_status_t moge_set_stage_events(void* const* events, int32_t n_events) {
+  if (!events || n_events == 0) {
+    g_record_stages = false;
+    return ok();
+  }
+  if (n_events != MOGE_STAGE_EVENTS)
+    return fail(MOGE_ERR_INVALID_ARG, "n_events=%d, expected %d", n_events, MOGE_STAGE_EVENTS);
+  for (int i = 0; i < MOGE_STAGE_EVENTS; ++i) {
+    if (!events[i]) return fail(MOGE_ERR_INVALID_ARG, "events[%d] is NULL", i);
+    g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_record_stages = true;
+  return ok();
+}
+
+const char* moge_last_error(void) { return g_last_error.c_str(); }
+
+size_t moge_workspace_size(const moge_dims_t* dims) {
+  const std::string saved = g_last_error;
+  const moge_status_t s = check_dims(dims);
+  g_last_error = saved;
+  if (s != MOGE_OK) return 0;
+  return make_plan(dims).total;
+}
+
+moge_status_t moge_route(const moge_dims_t* dims, const float* logits, float* probs,
+                         int32_t* topk_idx, float* topk_gate, void* stream) {
+  CHECK(check_dims(dims));
+  CHECK(check_ptr(logits, 4, "logits", true));
+  CHECK(check_ptr(probs, 4, "probs", false));
+  CHECK(check_ptr(topk_idx, 4, "topk_idx", true));
+  CHECK(check_ptr(topk_gate, 4, "topk_gate", true));
+  if (dims->T == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  CHECK(hip_check(moge::launch_route(logits, 1, dims->T, dims->N, dims->M, dims->k_per_group,
+                                     nullptr, nullptr, probs, topk_idx, topk_gate, st),
+                  "moge_route"));
+  return ok();
+}
+
+moge_status_t moge_permute(const moge_dims_t* dims, const int32_t* topk_idx, const void* x,
+                           int32_t* counts, int32_t* offsets, int32_t* group_counts,
+                           int32_t* sorted_pair, int32_t* pair_row, void* x_perm, void* ws,
+                           size_t ws_bytes, void* stream) {
+  CHECK(check_dims(dims));
+  CHECK(check_ptr(topk_idx, 4, "topk_idx", true));
+  CHECK(check_ptr(counts, 4, "counts", true));
+  CHECK(check_ptr(offsets, 4, "offsets", true));
+  CHECK(check_ptr(group_counts, 4, "group_counts", true));
+  CHECK(check_ptr(sorted_pair, 4, "sorted_pair", true));
+  CHECK(check_ptr(pair_row, 4, "pair_row", true));
+  CHECK(check_ptr(x_perm, 16, "x_perm", false));
+  CHECK(check_ptr(x, 16, "x", x_perm != nullptr));
+  Plan p;
+  CHECK(check_ws(dims, ws, ws_bytes, &p));
+  if (dims->T == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int K = dims->M * dims->k_per_group;
+  CHECK(hip_check(moge::launch_permute(topk_idx, dims->T, K, dims->N, dims->M,
+                                       at<int32_t>(ws, p.blk_cnt), at<int32_t>(ws, p.blk_base),
+                                       counts, offsets, group_counts, sorted_pair, pair_row, st),
+                  "moge_permute"));
+  if (x_perm)
+    CHECK(hip_check(moge::launch_gather_rows(dims->dtype, x, sorted_pair, offsets + dims->N,
+                                             dims->T * K, K, dims->d, x_perm, st),
+                    "moge_permute gather"));
+  return ok();
+}
+
+moge_status_t moge_expert_ffn(const moge_dims_t* dims, const void* x_perm,
+                              const int32_t* offsets, const void* w_gate, const void* w_up,
+                              const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
+                              void* stream) {
+  CHECK(check_dims(dims));
+  CHECK(check_ptr(x_perm, 16, "x_perm", true));
+  CHECK(check_ptr(offsets, 4, "offsets", true));
+  CHECK(check_ptr(w_gate, 16, "w_gate", true));
+  CHECK(check_ptr(w_up, 16, "w_up", true));
+  CHECK(check_ptr(w_down, 16, "w_down", true));
+  CHECK(check_ptr(y_perm, 16, "y_perm", true));
+  Plan p;
+  CHECK(check_ws(dims, ws, ws_bytes, &p));
+  if (dims->T == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int K = dims->M * dims->k_per_group;
+  moge::FfnSeg g;
+  g.x = x_perm;
+  g.offsets = offsets;
+  g.rows = dims->T * K;
+  g.n_exp = dims->N;
+  g.inter = dims->inter;
+  g.w_gate = w_gate;
+  g.w_up = w_up;
+  g.w_down = w_down;
+  g.h = at<char>(ws, p.h);
+  g.y = y_perm;
+  CHECK(hip_check(moge::launch_ffn_gateup(dims->dtype, dims->d, g, nullptr, st),
+                  "moge_expert_ffn gate/up"));
+  CHECK(hip_check(moge::launch_ffn_down(dims->dtype, dims->d, g, nullptr, st),
+                  "moge_expert_ffn down"));
+  return ok();
+}
+
+moge_status_t moge_combine(const moge_dims_t* dims, const void* y_perm, const int32_t* pair_row,
+                           const float* topk_gate, const void* shared_out, void* y,
+                           void* stream) {
+  CHECK(check_dims(dims));
+  CHECK(check_ptr(y_perm, 16, "y_perm", true));
+  CHECK(check_ptr(pair_row, 4, "pair_row", true));
+  CHECK(check_ptr(topk_gate, 4, "topk_gate", true));
+  CHECK(check_ptr(shared_out, 16, "shared_out", false));
+  CHECK(check_ptr(y, 16, "y", true));
+  if (dims->T == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  CHECK(hip_check(moge::launch_combine(dims->dtype, dims->T, dims->M * dims->k_per_group, dims->d,
+                                       y_perm, pair_row, topk_gate, shared_out, y, st),
+                  "moge_combine"));
+  return ok();
+}
+
+moge_status_t moge_layer_forward(const moge_dims_t* dims, const void* x, const void* w_router,
+                                 const float* router_bias, const void* w_gate, const void* w_up,
+                                 const void* w_down, const void* ws_gate, const void* ws_up,
+                                 const void* ws_down, const float* logits_in, void* y,
+                                 float* logits_out, int32_t* topk_idx_out, float* topk_gate_out,
+                                 int32_t* group_counts_out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  CHECK(check_dims(dims));
+  const bool shared = dims->shared_inter > 0;
+  CHECK(check_ptr(x, 16, "x", true));
+  CHECK(check_ptr(logits_in, 4, "logits_in", false));
+  CHECK(check_ptr(w_router, 16, "w_router", logits_in == nullptr));
+  CHECK(check_ptr(router_bias, 4, "router_bias", false));
+  CHECK(check_ptr(w_gate, 16, "w_gate", true));
+  CHECK(check_ptr(w_up, 16, "w_up", true));
+  CHECK(check_ptr(w_down, 16, "w_down", true));
+  CHECK(check_ptr(ws_gate, 16, "ws_gate", shared));
+  CHECK(check_ptr(ws_up, 16, "ws_up", shared));
+  CHECK(check_ptr(ws_down, 16, "ws_down", shared));
+  CHECK(check_ptr(y, 16, "y", true));
+  CHECK(check_ptr(logits_out, 4, "logits_out", false));
+  CHECK(check_ptr(topk_idx_out, 4, "topk_idx_out", false));
+  CHECK(check_ptr(topk_gate_out, 4, "topk_gate_out", false));
+  CHECK(check_ptr(group_counts_out, 4, "group_counts_out", false));
+  Plan p;
+  CHECK(check_ws(dims, ws, ws_bytes, &p));
+  if (dims->T == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int T = dims->T, N = dims->N, M = dims->M, kp = dims->k_per_group, K = M * kp;
+  const int R = T * K;
+
+  mark(0, st);
+  // S0 router scores (split contraction, partial sums added by the routing kernel)
+  const float* scores = logits_in;
+  const float* bias = nullptr;
+  int ksplit = 1;
+  if (!logits_in) {
+    float* partial = at<float>(ws, p.partial);
+    CHECK(hip_check(moge::launch_router_scores(dims->dtype, x, w_router, T, dims->d, N, p.ksplit,
+                                               partial, st),
+                    "router scores"));
+    scores = partial;
+    bias = router_bias;
+    ksplit = p.ksplit;
+  }
+  mark(1, st);
+  // S1+S2 softmax and grouped top-K'
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, p.idx);
+  float* gate = topk_gate_out ? topk_gate_out : at<float>(ws, p.gate);
+  CHECK(hip_check(moge::launch_route(scores, ksplit, T, N, M, kp, bias, logits_out, nullptr, idx,
+                                     gate, st),
+                  "route"));
+  mark(2, st);
+  // S3 permutation (the FFN gathers its rows from x through sorted_pair)
+  int32_t* gcounts = group_counts_out ? group_counts_out : at<int32_t>(ws, p.gcounts);
+  int32_t* offsets = at<int32_t>(ws, p.offsets);
+  int32_t* sorted_pair = at<int32_t>(ws, p.sorted_pair);
+  int32_t* pair_row = at<int32_t>(ws, p.pair_row);
+  CHECK(hip_check(moge::launch_permute(idx, T, K, N, M, at<int32_t>(ws, p.blk_cnt),
+                                       at<int32_t>(ws, p.blk_base), at<int32_t>(ws, p.counts),
+                                       offsets, gcounts, sorted_pair, pair_row, st),
+                  "permute"));
+  mark(3, st);
+  // S4-S6 routed and shared SwiGLU experts, one launch per projection
+  moge::FfnSeg routed;
+  routed.x = x;
+  routed.row_src = sorted_pair;
+  routed.row_div = K;
+  routed.offsets = offsets;
+  routed.rows = R;
+  routed.n_exp = N;
+  routed.inter = dims->inter;
+  routed.w_gate = w_gate;
+  routed.w_up = w_up;
+  routed.w_down = w_down;
+  routed.h = at<char>(ws, p.h);
+  routed.y = at<char>(ws, p.y_perm);
+  moge::FfnSeg sh;
+  if (shared) {
+    sh.x = x;
+    sh.rows = T;
+    sh.n_exp = 1;
+    sh.inter = dims->shared_inter;
+    sh.w_gate = ws_gate;
+    sh.w_up = ws_up;
+    sh.w_down = ws_down;
+    sh.h = at<char>(ws, p.hs);
+    sh.y = at<char>(ws, p.sh);
+  }
+  CHECK(hip_check(moge::launch_ffn_gateup(dims->dtype, dims->d, routed, shared ? &sh : nullptr, st),
+                  "expert gate/up"));
+  mark(4, st);
+  CHECK(hip_check(moge::launch_ffn_down(dims->dtype, dims->d, routed, shared ? &sh : nullptr, st),
+                  "expert down"));
+  mark(5, st);
+  // S7 combine
+  CHECK(hip_check(moge::launch_combine(dims->dtype, T, K, dims->d, routed.y, pair_row, gate,
+                                       shared ? sh.y : nullptr, y, st),
+                  "combine"));
+  mark(6, st);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Device-side helpers shared by the MoGE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moge {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Eight consecutive elements along the contraction dimension: the per-lane share
+// of one K=32 step of a 16x16 MFMA tile.  bf16: 16 bytes, one v_mfma 16x16x32.
+// float: 32 bytes, eight v_mfma 16x16x4 (element j of every lane feeds the j-th
+// instruction; A and B use the same element->k assignment, so the sum over the 32
+// k values is complete whatever the order).
+// ---------------------------------------------------------------------------
+template <typename E> struct Frag8;
+
+template <> struct Frag8<bf16> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void load_nt(const bf16* p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  __device__ __forceinline__ void zero() { v = u32x4{0u, 0u, 0u, 0u}; }
+};
+
+template <> struct Frag8<float> {
+  f32x4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = *reinterpret_cast<const f32x4*>(p);
+    hi = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+  }
+  __device__ __forceinline__ void zero() {
+    lo = f32x4{0.f, 0.f, 0.f, 0.f};
+    hi = lo;
+  }
+};
+
+// acc[16x16] += A[16x32] * B[32x16]; lane l supplies row (l%16) of A and column
+// (l%16) of B, k-elements 8*(l/16)..8*(l/16)+7.  Result: lane l, register i holds
+// D[4*(l/16)+i][l%16].
+__device__ __forceinline__ f32x4 mfma_step(const Frag8<bf16>& a, const Frag8<bf16>& b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                 __builtin_bit_cast(bf16x8, b.v), acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_step(const Frag8<float>& a, const Frag8<float>& b, f32x4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[0], b.lo[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[1], b.lo[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[2], b.lo[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[3], b.lo[3], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[0], b.hi[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[1], b.hi[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[2], b.hi[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[3], b.hi[3], acc, 0, 0, 0);
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// element conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+template <typename E> __device__ __forceinline__ E from_f32(float v);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+
+// store four consecutive results (16 B float, 8 B bf16)
+__device__ __forceinline__ void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store4(bf16* p, f32x4 v) {
+  bf16x4 b;
+  b[0] = static_cast<bf16>(v[0]);
+  b[1] = static_cast<bf16>(v[1]);
+  b[2] = static_cast<bf16>(v[2]);
+  b[3] = static_cast<bf16>(v[3]);
+  *reinterpret_cast<bf16x4*>(p) = b;
+}
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+
+// ---------------------------------------------------------------------------
+// wave reductions (fixed butterfly order: deterministic)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = threadIdx.x & (kWave - 1);
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+}  // namespace moge

@@ -1,0 +1,61 @@
+// Internal launch interface of the MoGE library (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moge {
+
+// ---- routing (router.hip) --------------------------------------------------
+// partial[ks][t][e] = sum over the ks-th contraction split of x[t,:] . w_r[e,:]
+hipError_t launch_router_scores(int dtype, const void* x, const void* w_router, int T, int d,
+                                int N, int ksplit, float* partial, hipStream_t st);
+// scores = sum_ks partial (+ bias); softmax over N; per-group top-K'.
+hipError_t launch_route(const float* partial, int ksplit, int T, int N, int M, int kp,
+                        const float* bias, float* logits_out, float* probs, int32_t* idx,
+                        float* gate, hipStream_t st);
+int router_ksplit(int T, int d, int N);
+
+// ---- permutation (permute.hip) ---------------------------------------------
+constexpr int kPermTokens = 64;  // tokens per permutation block (one wave)
+inline int perm_blocks(int T) { return (T + kPermTokens - 1) / kPermTokens; }
+hipError_t launch_permute(const int32_t* idx, int T, int K, int N, int M, int32_t* blk_cnt,
+                          int32_t* blk_base, int32_t* counts, int32_t* offsets,
+                          int32_t* group_counts, int32_t* sorted_pair, int32_t* pair_row,
+                          hipStream_t st);
+// rows at or past *offsets_end (the device-side total row count) are left untouched
+hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* sorted_pair,
+                              const int32_t* offsets_end, int R, int K, int d, void* x_perm,
+                              hipStream_t st);
+
+// ---- expert FFN (ffn.hip) --------------------------------------------------
+// One segment = a set of SwiGLU experts sharing a weight layout.  Row r of the
+// segment reads activation row x[row_src ? row_src[r] / row_div : r].  Expert e
+// owns rows offsets[e] .. offsets[e+1]; offsets == nullptr means a single expert
+// owning rows [0, rows).
+struct FfnSeg {
+  const void* x = nullptr;
+  const int32_t* row_src = nullptr;
+  int row_div = 1;
+  const int32_t* offsets = nullptr;
+  int rows = 0;
+  int n_exp = 0;
+  int inter = 0;
+  const void* w_gate = nullptr;  // [n_exp, inter, d]
+  const void* w_up = nullptr;    // [n_exp, inter, d]
+  const void* w_down = nullptr;  // [n_exp, d, inter]
+  void* h = nullptr;             // [rows, inter] dtype (gate/up output, down input)
+  void* y = nullptr;             // [rows, d] dtype
+};
+// gate/up + SwiGLU for up to two segments in one launch (routed + shared)
+hipError_t launch_ffn_gateup(int dtype, int d, const FfnSeg& a, const FfnSeg* b, hipStream_t st);
+// down projection for up to two segments in one launch
+hipError_t launch_ffn_down(int dtype, int d, const FfnSeg& a, const FfnSeg* b, hipStream_t st);
+
+// ---- combine (combine.hip) -------------------------------------------------
+hipError_t launch_combine(int dtype, int T, int K, int d, const void* y_perm,
+                          const int32_t* pair_row, const float* gate, const void* shared,
+                          void* y, hipStream_t st);
+
+}  // namespace moge

@@ -1,0 +1,167 @@
+// Router: scores x W_r^T (+b), global softmax over all experts, per-group top-K'.
+//
+// Grouped routing as the TechWalker page describes it (section 一 创新架构): the
+// softmax runs over every routed expert first; then each of the M equal groups
+// keeps its own K' best experts, so every group receives the same number of
+// (token, expert) pairs.  The Reportify concept page (技术创新细节) states the same:
+// each group routes its top-K independently, and the load difference between
+// groups is zero.
+#include "moge_common.hpp"
+#include "moge_internal.hpp"
+
+namespace moge {
+
+// ---------------------------------------------------------------------------
+// scores: one wave per (16 experts x 16 tokens) tile and contraction split.
+// A operand = router weight rows (experts), B operand = token rows; the MFMA
+// result D[expert][token] leaves four consecutive experts of one token per lane.
+// Splitting the contraction gives the small-T (decode) case enough waves; the
+// partial sums are added in a fixed order by the routing kernel.
+// ---------------------------------------------------------------------------
+template <typename E>
+__global__ __launch_bounds__(64) void k_router_scores(const E* __restrict__ x,
+                                                      const E* __restrict__ wr, int T, int d,
+                                                      int N, int steps_per_split,
+                                                      float* __restrict__ partial) {
+  const int l = threadIdx.x;
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16, ks = blockIdx.z;
+  const int nsteps = d / 32;
+  const int s0 = ks * steps_per_split;
+  const int s1 = min(nsteps, s0 + steps_per_split);
+  const int ln = l & 15, kq = (l >> 4) * 8;
+  const E* pa = wr + (size_t)min(e0 + ln, N - 1) * d + kq;
+  const E* pb = x + (size_t)min(t0 + ln, T - 1) * d + kq;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = s0; s < s1; ++s) {
+    Frag8<E> a, b;
+    a.load(pa + s * 32);
+    b.load(pb + s * 32);
+    acc = mfma_step(a, b, acc);
+  }
+  const int t = t0 + ln;
+  if (t < T) {
+    float* out = partial + ((size_t)ks * T + t) * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + 4 * (l >> 4) + i;
+      if (e < N) out[e] = acc[i];
+    }
+  }
+}
+
+int router_ksplit(int T, int d, int N) {
+  const int tiles = ((T + 15) / 16) * ((N + 15) / 16);
+  const int nsteps = d / 32;
+  int ks = 2048 / (tiles > 0 ? tiles : 1);
+  if (ks < 1) ks = 1;
+  if (ks > nsteps) ks = nsteps;
+  if (ks > 64) ks = 64;
+  return ks;
+}
+
+hipError_t launch_router_scores(int dtype, const void* x, const void* w_router, int T, int d,
+                                int N, int ksplit, float* partial, hipStream_t st) {
+  const int nsteps = d / 32;
+  const int per = (nsteps + ksplit - 1) / ksplit;
+  dim3 grid((N + 15) / 16, (T + 15) / 16, ksplit);
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_router_scores<bf16>, grid, dim3(64), 0, st, (const bf16*)x,
+                       (const bf16*)w_router, T, d, N, per, partial);
+  else
+    hipLaunchKernelGGL(k_router_scores<float>, grid, dim3(64), 0, st, (const float*)x,
+                       (const float*)w_router, T, d, N, per, partial);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// routing: one wave per token, lane j holds experts j, j+64, j+128, j+192.
+// Selection compares float32 scores only (exact); equal scores go to the lower
+// expert index because a candidate replaces the current best only when strictly
+// greater while experts are visited in increasing index order.
+// ---------------------------------------------------------------------------
+constexpr int kRouteWaves = 4;
+
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ partial, int ksplit,
+                                               int T, int N, int M, int kp,
+                                               const float* __restrict__ bias,
+                                               float* __restrict__ logits_out,
+                                               float* __restrict__ probs,
+                                               int32_t* __restrict__ idx,
+                                               float* __restrict__ gate) {
+  __shared__ float s_l[kRouteWaves][256];
+  __shared__ float s_p[kRouteWaves][256];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int t = blockIdx.x * kRouteWaves + w;
+  const bool valid = t < T;
+  const int tt = valid ? t : 0;
+
+  float v[4], ex[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = l + 64 * j;
+    v[j] = -INFINITY;
+    if (e < N) {
+      // start from split 0 (not from 0.f) so a lone -0.0 score keeps its sign
+      float s = partial[(size_t)tt * N + e];
+      for (int ks = 1; ks < ksplit; ++ks) s += partial[((size_t)ks * T + tt) * N + e];
+      if (bias) s += bias[e];
+      v[j] = s;
+      mx = fmaxf(mx, s);
+    }
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = l + 64 * j;
+    ex[j] = (e < N) ? expf(v[j] - mx) : 0.f;
+    sum += ex[j];
+  }
+  sum = wave_sum(sum);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = l + 64 * j;
+    if (e < N) {
+      const float p = ex[j] / sum;
+      s_l[w][e] = v[j];
+      s_p[w][e] = p;
+      if (valid && logits_out) logits_out[(size_t)t * N + e] = v[j];
+      if (valid && probs) probs[(size_t)t * N + e] = p;
+    }
+  }
+  __syncthreads();
+  if (!valid) return;
+  const int G = N / M, K = M * kp;
+  for (int g = l; g < M; g += 64) {
+    uint64_t taken[4] = {0ull, 0ull, 0ull, 0ull};
+    for (int j = 0; j < kp; ++j) {
+      int bi = -1;
+      float bv = 0.f;
+      for (int q = 0; q < G; ++q) {
+        if ((taken[q >> 6] >> (q & 63)) & 1ull) continue;
+        const float s = s_l[w][g * G + q];
+        if (bi < 0 || s > bv) {
+          bv = s;
+          bi = q;
+        }
+      }
+      taken[bi >> 6] |= 1ull << (bi & 63);
+      const int e = g * G + bi;
+      idx[(size_t)t * K + g * kp + j] = e;
+      gate[(size_t)t * K + g * kp + j] = s_p[w][e];
+    }
+  }
+}
+
+hipError_t launch_route(const float* partial, int ksplit, int T, int N, int M, int kp,
+                        const float* bias, float* logits_out, float* probs, int32_t* idx,
+                        float* gate, hipStream_t st) {
+  dim3 grid((T + kRouteWaves - 1) / kRouteWaves);
+  hipLaunchKernelGGL(k_route, grid, dim3(64 * kRouteWaves), 0, st, partial, ksplit, T, N, M, kp,
+                     bias, logits_out, probs, idx, gate);
+  return hipGetLastError();
+}
+
+}  // namespace moge

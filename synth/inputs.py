@@ -109,20 +109,14 @@ class LayerInputs:
         return self.cfg.dtype == "bf16"
 
 
-def make_layer_inputs(cfg: LayerConfig, T: Optional[int] = None,
-                      seed: Optional[int] = None) -> LayerInputs:
-    """All tensors of one layer call, seeded.  T overrides cfg.T (the weights do
-    not depend on T; x's first rows do not either, since x is drawn row-major)."""
-    T = cfg.T if T is None else T
+def make_weights(cfg: LayerConfig, seed: Optional[int] = None) -> dict:
+    """The layer's weights (they do not depend on T)."""
     seed = cfg.seed if seed is None else seed
     dt = cfg.dtype
     d, N, I, Is = cfg.d, cfg.N, cfg.inter, cfg.I_s
-    bias = zipf_bias(N, cfg.zipf_s) if cfg.zipf_s > 0 else None
-    return LayerInputs(
-        cfg=cfg,
-        x=normal_tensor((T, d), cfg.x_std, seed, TID_X, dt),
+    return dict(
         w_router=normal_tensor((N, d), cfg.router_std, seed, TID_WR, dt),
-        router_bias=bias,
+        router_bias=zipf_bias(N, cfg.zipf_s) if cfg.zipf_s > 0 else None,
         w_gate=normal_tensor((N, I, d), cfg.w_std, seed, TID_WG, dt),
         w_up=normal_tensor((N, I, d), cfg.w_std, seed, TID_WU, dt),
         w_down=normal_tensor((N, d, I), cfg.w_std, seed, TID_WD, dt),
@@ -130,6 +124,25 @@ def make_layer_inputs(cfg: LayerConfig, T: Optional[int] = None,
         ws_up=normal_tensor((Is, d), cfg.w_std, seed, TID_WSU, dt),
         ws_down=normal_tensor((d, Is), cfg.w_std, seed, TID_WSD, dt),
     )
+
+
+def make_x(cfg: LayerConfig, T: Optional[int] = None, seed: Optional[int] = None) -> np.ndarray:
+    """Activations x[T,d]; row t does not depend on T (drawn row-major)."""
+    T = cfg.T if T is None else T
+    seed = cfg.seed if seed is None else seed
+    return normal_tensor((T, cfg.d), cfg.x_std, seed, TID_X, cfg.dtype)
+
+
+def make_layer_inputs(cfg: LayerConfig, T: Optional[int] = None,
+                      seed: Optional[int] = None, weights: Optional[dict] = None) -> LayerInputs:
+    """All tensors of one layer call, seeded.  T overrides cfg.T.  `weights` may
+    pass in a make_weights() result to avoid drawing the weights again."""
+    w = make_weights(cfg, seed) if weights is None else weights
+    if cfg.zipf_s > 0:
+        w = dict(w, router_bias=zipf_bias(cfg.N, cfg.zipf_s))
+    else:
+        w = dict(w, router_bias=None)
+    return LayerInputs(cfg=cfg, x=make_x(cfg, T, seed), **w)
 
 
 def make_scores(cfg: LayerConfig, T: Optional[int] = None, seed: Optional[int] = None,
