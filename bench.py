@@ -47,6 +47,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="C1", help="workload: C0..C4 (default C1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--row-major", action="store_true",
+                    help="time moge_layer_forward on the row-major weights instead of "
+                         "moge_layer_forward_packed")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the CPU oracle sample (default: the whole batch, max 64)")
     return ap.parse_args()
@@ -160,13 +163,21 @@ def main() -> int:
     y = torch.empty((cfg.T, cfg.d), dtype=tdt, device="cuda")
     idx = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda")
     gc = torch.empty((cfg.M,), dtype=torch.int32, device="cuda")
+    # weights are parameters: packed once, outside the timed region
+    packed = torch.empty(moge.packed_weights_size(dims), dtype=torch.uint8, device="cuda")
+    moge.pack_weights(dims, w["w_gate"], w["w_up"], w["w_down"], w["ws_gate"], w["ws_up"],
+                      w["ws_down"], packed)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
     def step():
-        moge.layer_forward(dims, x, w["w_router"], w["router_bias"], w["w_gate"], w["w_up"],
-                           w["w_down"], w["ws_gate"], w["ws_up"], w["ws_down"], y, ws,
-                           topk_idx_out=idx, group_counts_out=gc)
+        if args.row_major:
+            moge.layer_forward(dims, x, w["w_router"], w["router_bias"], w["w_gate"], w["w_up"],
+                               w["w_down"], w["ws_gate"], w["ws_up"], w["ws_down"], y, ws,
+                               topk_idx_out=idx, group_counts_out=gc)
+        else:
+            moge.layer_forward_packed(dims, x, w["w_router"], w["router_bias"], packed, y, ws,
+                                      topk_idx_out=idx, group_counts_out=gc)
 
     for _ in range(args.warmup):
         step()
@@ -223,7 +234,8 @@ def main() -> int:
         "dtype": cfg.dtype, "data": "synthetic (seeded N(0,std) inputs, random-init weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "N": cfg.N, "M": cfg.M,
                    "k_per_group": cfg.kp, "inter": cfg.inter, "shared_experts": cfg.n_shared,
-                   "shared_inter_total": cfg.I_s, "parallelism": "single GPU"},
+                   "shared_inter_total": cfg.I_s, "parallelism": "single GPU",
+                   "weights": "row-major" if args.row_major else "packed"},
         "roofline": {"bound": bound, "kernel": "gate_up+SwiGLU (routed+shared)",
                      "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -163,13 +163,52 @@ moge_status_t moge_layer_forward(const moge_dims_t* dims, const void* x, const v
                                  int32_t* group_counts_out, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* Packed expert weights.  The layer's throughput at decode batch sizes is the
+ * rate at which the expert weights stream from HBM.  Read in their row-major
+ * layout, every load of the MFMA fragment a wave needs (16 weight rows x 32
+ * contraction elements) touches 16 rows 64 bytes at a time; in the packed layout
+ * that fragment is 512 contiguous elements and a wave's whole weight stream is one
+ * contiguous range.  Pack once (weights are parameters), then run
+ * moge_layer_forward_packed; results are bit-identical to moge_layer_forward.
+ *
+ * Layout: fragment tile = 16 rows x 32 contraction elements stored as 64 chunks of
+ * 8 consecutive contraction elements; chunk l holds row l % 16, elements
+ * 8*(l/16) .. 8*(l/16)+7.  Gate/up part of an expert: for row block b < I/16 and
+ * step s < d/32, the gate tile then the up tile of rows 16b..16b+15, at tile index
+ * (b*(d/32) + s)*2 + {0,1}.  Down part: for row block b < d/32 (32 rows) and step
+ * s < I/32, the tiles of rows 32b..32b+15 and 32b+16..32b+31 at tile index
+ * (b*(I/32) + s)*2 + {0,1}.  Buffer order: routed gate/up parts of experts 0..N-1,
+ * routed down parts of experts 0..N-1, shared gate/up part, shared down part.
+ * Its size equals the total size of the six row-major weight tensors. */
+
+/* Bytes of the packed weight buffer for these dims; 0 if the dims are invalid. */
+size_t moge_packed_weights_size(const moge_dims_t* dims);
+
+/* Write the packed layout of the six row-major weight tensors into `packed`
+ * (device, 256-byte aligned, >= moge_packed_weights_size bytes, caller-owned). A
+ * pure copy; asynchronous on `stream`. */
+moge_status_t moge_pack_weights(const moge_dims_t* dims, const void* w_gate, const void* w_up,
+                                const void* w_down, const void* ws_gate, const void* ws_up,
+                                const void* ws_down, void* packed, size_t packed_bytes,
+                                void* stream);
+
+/* moge_layer_forward with the expert weights taken from a moge_pack_weights
+ * buffer (same arguments otherwise; same results, bit for bit). */
+moge_status_t moge_layer_forward_packed(const moge_dims_t* dims, const void* x,
+                                        const void* w_router, const float* router_bias,
+                                        const void* packed, const float* logits_in, void* y,
+                                        float* logits_out, int32_t* topk_idx_out,
+                                        float* topk_gate_out, int32_t* group_counts_out,
+                                        void* ws, size_t ws_bytes, void* stream);
+
 /* Stage timing for profiling.  events: MOGE_STAGE_EVENTS hipEvent_t handles
  * (passed as void*) created by the caller; moge_layer_forward then records
  * events[0] before its first kernel and events[i] after stage i on its stream:
  * 1 router scores, 2 softmax + grouped top-K', 3 permutation, 4 gate/up + SwiGLU
  * (routed and shared), 5 down projection (routed and shared), 6 combine.
  * events == NULL or n_events == 0 turns recording off.  The setting belongs to
- * the calling thread.  Any other n_events -> MOGE_ERR_INVALID_ARG. */
+ * the calling thread.  Any other n_events -> MOGE_ERR_INVALID_ARG.  Both
+ * moge_layer_forward and moge_layer_forward_packed record them. */
 #define MOGE_STAGE_EVENTS 7
 moge_status_t moge_set_stage_events(void* const* events, int32_t n_events);
 

@@ -65,6 +65,11 @@ _SIGS = {
     "moge_layer_forward": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moge_set_stage_events": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.c_int32]),
+    "moge_packed_weights_size": (ctypes.c_size_t, [ctypes.POINTER(Dims)]),
+    "moge_pack_weights": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_size_t, _P]),
+    "moge_layer_forward_packed": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P,
+                                                 _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
 }
 STAGE_EVENTS = 7
 STAGE_NAMES = ("router_scores", "route", "permute", "gate_up", "down", "combine")
@@ -171,3 +176,26 @@ def set_stage_events(events) -> None:
         return
     arr = (_P * len(events))(*events)
     _check(lib.moge_set_stage_events(arr, len(events)), "moge_set_stage_events")
+
+
+def packed_weights_size(dims: Dims) -> int:
+    return int(lib.moge_packed_weights_size(ctypes.byref(dims)))
+
+
+def pack_weights(dims: Dims, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, packed,
+                 stream=None) -> None:
+    _check(lib.moge_pack_weights(ctypes.byref(dims), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                 _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(packed),
+                                 packed.numel() * packed.element_size(), _stream(stream)),
+           "moge_pack_weights")
+
+
+def layer_forward_packed(dims: Dims, x, w_router, router_bias, packed, y, ws, logits_in=None,
+                         logits_out=None, topk_idx_out=None, topk_gate_out=None,
+                         group_counts_out=None, stream=None) -> None:
+    _check(lib.moge_layer_forward_packed(ctypes.byref(dims), _ptr(x), _ptr(w_router),
+                                         _ptr(router_bias), _ptr(packed), _ptr(logits_in), _ptr(y),
+                                         _ptr(logits_out), _ptr(topk_idx_out),
+                                         _ptr(topk_gate_out), _ptr(group_counts_out), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)),
+           "moge_layer_forward_packed")

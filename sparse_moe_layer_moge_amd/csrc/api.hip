@@ -9,6 +9,7 @@
 
 #include "../../include/moge.h"
 #include "moge_internal.hpp"
+#include "packed_layout.hpp"
 
 namespace {
 
@@ -69,6 +70,15 @@ moge_status_t check_dims(const moge_dims_t* d) {
                 d->d, d->inter, d->shared_inter);
   if ((long long)d->T * K >= (1ll << 31))
     return fail(MOGE_ERR_UNSUPPORTED, "T*K=%lld rows exceed int32", (long long)d->T * K);
+  // activation-side buffers are addressed with 32-bit byte offsets
+  const long long R = (long long)d->T * K, es = esize(d);
+  long long widest = R * d->d;
+  if (R * d->inter > widest) widest = R * d->inter;
+  if ((long long)d->T * d->shared_inter > widest) widest = (long long)d->T * d->shared_inter;
+  if ((long long)d->inter * d->d > widest) widest = (long long)d->inter * d->d;
+  if (widest * es > 0xFFFFFFFFll)
+    return fail(MOGE_ERR_UNSUPPORTED, "an activation or expert buffer exceeds 4 GiB (%lld bytes)",
+                widest * es);
   return MOGE_OK;
 }
 
@@ -141,6 +151,114 @@ moge_status_t check_ws(const moge_dims_t* d, void* ws, size_t ws_bytes, Plan* pl
   if (ws_bytes < plan->total)
     return fail(MOGE_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, plan->total);
   return MOGE_OK;
+}
+
+struct Weights {
+  const void *gate = nullptr, *up = nullptr, *down = nullptr;        // row-major routed
+  const void *s_gate = nullptr, *s_up = nullptr, *s_down = nullptr;  // row-major shared
+  const void *p_gu = nullptr, *p_down = nullptr;                     // packed routed
+  const void *ps_gu = nullptr, *ps_down = nullptr;                   // packed shared
+};
+
+// The whole layer on one stream; `w` holds either row-major or packed weights
+// (pointers already checked by the caller).
+moge_status_t layer_impl(const moge_dims_t* dims, const void* x, const void* w_router,
+                         const float* router_bias, const Weights& w, const float* logits_in,
+                         void* y, float* logits_out, int32_t* topk_idx_out, float* topk_gate_out,
+                         int32_t* group_counts_out, void* ws, size_t ws_bytes, void* stream) {
+  const bool shared = dims->shared_inter > 0;
+  CHECK(check_ptr(x, 16, "x", true));
+  CHECK(check_ptr(logits_in, 4, "logits_in", false));
+  CHECK(check_ptr(w_router, 16, "w_router", logits_in == nullptr));
+  CHECK(check_ptr(router_bias, 4, "router_bias", false));
+  CHECK(check_ptr(y, 16, "y", true));
+  CHECK(check_ptr(logits_out, 4, "logits_out", false));
+  CHECK(check_ptr(topk_idx_out, 4, "topk_idx_out", false));
+  CHECK(check_ptr(topk_gate_out, 4, "topk_gate_out", false));
+  CHECK(check_ptr(group_counts_out, 4, "group_counts_out", false));
+  Plan p;
+  CHECK(check_ws(dims, ws, ws_bytes, &p));
+  if (dims->T == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int T = dims->T, N = dims->N, M = dims->M, kp = dims->k_per_group, K = M * kp;
+  const int R = T * K;
+
+  mark(0, st);
+  // S0 router scores (split contraction, partial sums added by the routing kernel)
+  const float* scores = logits_in;
+  const float* bias = nullptr;
+  int ksplit = 1;
+  if (!logits_in) {
+    float* partial = at<float>(ws, p.partial);
+    CHECK(hip_check(moge::launch_router_scores(dims->dtype, x, w_router, T, dims->d, N, p.ksplit,
+                                               partial, st),
+                    "router scores"));
+    scores = partial;
+    bias = router_bias;
+    ksplit = p.ksplit;
+  }
+  mark(1, st);
+  // S1+S2 softmax and grouped top-K'
+  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, p.idx);
+  float* gate = topk_gate_out ? topk_gate_out : at<float>(ws, p.gate);
+  CHECK(hip_check(moge::launch_route(scores, ksplit, T, N, M, kp, bias, logits_out, nullptr, idx,
+                                     gate, st),
+                  "route"));
+  mark(2, st);
+  // S3 permutation (the FFN gathers its rows from x through sorted_pair)
+  int32_t* gcounts = group_counts_out ? group_counts_out : at<int32_t>(ws, p.gcounts);
+  int32_t* offsets = at<int32_t>(ws, p.offsets);
+  int32_t* sorted_pair = at<int32_t>(ws, p.sorted_pair);
+  int32_t* pair_row = at<int32_t>(ws, p.pair_row);
+  CHECK(hip_check(moge::launch_permute(idx, T, K, N, M, at<int32_t>(ws, p.blk_cnt),
+                                       at<int32_t>(ws, p.blk_base), at<int32_t>(ws, p.counts),
+                                       offsets, gcounts, sorted_pair, pair_row, st),
+                  "permute"));
+  mark(3, st);
+  // S4-S6 routed and shared SwiGLU experts, one launch per projection
+  moge::FfnSeg routed;
+  routed.x = x;
+  routed.x_rows = T;
+  routed.row_src = sorted_pair;
+  routed.row_div = K;
+  routed.offsets = offsets;
+  routed.rows = R;
+  routed.n_exp = N;
+  routed.inter = dims->inter;
+  routed.w_gate = w.gate;
+  routed.w_up = w.up;
+  routed.w_down = w.down;
+  routed.p_gu = w.p_gu;
+  routed.p_down = w.p_down;
+  routed.h = at<char>(ws, p.h);
+  routed.y = at<char>(ws, p.y_perm);
+  moge::FfnSeg sh;
+  if (shared) {
+    sh.x = x;
+    sh.x_rows = T;
+    sh.rows = T;
+    sh.n_exp = 1;
+    sh.inter = dims->shared_inter;
+    sh.w_gate = w.s_gate;
+    sh.w_up = w.s_up;
+    sh.w_down = w.s_down;
+    sh.p_gu = w.ps_gu;
+    sh.p_down = w.ps_down;
+    sh.h = at<char>(ws, p.hs);
+    sh.y = at<char>(ws, p.sh);
+  }
+  CHECK(hip_check(moge::launch_ffn_gateup(dims->dtype, dims->d, routed, shared ? &sh : nullptr, st),
+                  "expert gate/up"));
+  mark(4, st);
+  CHECK(hip_check(moge::launch_ffn_down(dims->dtype, dims->d, routed, shared ? &sh : nullptr, st),
+                  "expert down"));
+  mark(5, st);
+  // S7 combine
+  CHECK(hip_check(moge::launch_combine(dims->dtype, T, K, dims->d, routed.y, pair_row, gate,
+                                       shared ? sh.y : nullptr, y, st),
+                  "combine"));
+  mark(6, st);
+  return ok();
 }
 
 }  // namespace
@@ -236,6 +354,7 @@ moge_status_t moge_expert_ffn(const moge_dims_t* dims, const void* x_perm,
   const int K = dims->M * dims->k_per_group;
   moge::FfnSeg g;
   g.x = x_perm;
+  g.x_rows = dims->T * K;
   g.offsets = offsets;
   g.rows = dims->T * K;
   g.n_exp = dims->N;
@@ -278,98 +397,85 @@ moge_status_t moge_layer_forward(const moge_dims_t* dims, const void* x, const v
                                  void* stream) {
   CHECK(check_dims(dims));
   const bool shared = dims->shared_inter > 0;
-  CHECK(check_ptr(x, 16, "x", true));
-  CHECK(check_ptr(logits_in, 4, "logits_in", false));
-  CHECK(check_ptr(w_router, 16, "w_router", logits_in == nullptr));
-  CHECK(check_ptr(router_bias, 4, "router_bias", false));
   CHECK(check_ptr(w_gate, 16, "w_gate", true));
   CHECK(check_ptr(w_up, 16, "w_up", true));
   CHECK(check_ptr(w_down, 16, "w_down", true));
   CHECK(check_ptr(ws_gate, 16, "ws_gate", shared));
   CHECK(check_ptr(ws_up, 16, "ws_up", shared));
   CHECK(check_ptr(ws_down, 16, "ws_down", shared));
-  CHECK(check_ptr(y, 16, "y", true));
-  CHECK(check_ptr(logits_out, 4, "logits_out", false));
-  CHECK(check_ptr(topk_idx_out, 4, "topk_idx_out", false));
-  CHECK(check_ptr(topk_gate_out, 4, "topk_gate_out", false));
-  CHECK(check_ptr(group_counts_out, 4, "group_counts_out", false));
-  Plan p;
-  CHECK(check_ws(dims, ws, ws_bytes, &p));
-  if (dims->T == 0) return ok();
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int T = dims->T, N = dims->N, M = dims->M, kp = dims->k_per_group, K = M * kp;
-  const int R = T * K;
+  Weights w;
+  w.gate = w_gate;
+  w.up = w_up;
+  w.down = w_down;
+  w.s_gate = ws_gate;
+  w.s_up = ws_up;
+  w.s_down = ws_down;
+  return layer_impl(dims, x, w_router, router_bias, w, logits_in, y, logits_out, topk_idx_out,
+                    topk_gate_out, group_counts_out, ws, ws_bytes, stream);
+}
 
-  mark(0, st);
-  // S0 router scores (split contraction, partial sums added by the routing kernel)
-  const float* scores = logits_in;
-  const float* bias = nullptr;
-  int ksplit = 1;
-  if (!logits_in) {
-    float* partial = at<float>(ws, p.partial);
-    CHECK(hip_check(moge::launch_router_scores(dims->dtype, x, w_router, T, dims->d, N, p.ksplit,
-                                               partial, st),
-                    "router scores"));
-    scores = partial;
-    bias = router_bias;
-    ksplit = p.ksplit;
-  }
-  mark(1, st);
-  // S1+S2 softmax and grouped top-K'
-  int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, p.idx);
-  float* gate = topk_gate_out ? topk_gate_out : at<float>(ws, p.gate);
-  CHECK(hip_check(moge::launch_route(scores, ksplit, T, N, M, kp, bias, logits_out, nullptr, idx,
-                                     gate, st),
-                  "route"));
-  mark(2, st);
-  // S3 permutation (the FFN gathers its rows from x through sorted_pair)
-  int32_t* gcounts = group_counts_out ? group_counts_out : at<int32_t>(ws, p.gcounts);
-  int32_t* offsets = at<int32_t>(ws, p.offsets);
-  int32_t* sorted_pair = at<int32_t>(ws, p.sorted_pair);
-  int32_t* pair_row = at<int32_t>(ws, p.pair_row);
-  CHECK(hip_check(moge::launch_permute(idx, T, K, N, M, at<int32_t>(ws, p.blk_cnt),
-                                       at<int32_t>(ws, p.blk_base), at<int32_t>(ws, p.counts),
-                                       offsets, gcounts, sorted_pair, pair_row, st),
-                  "permute"));
-  mark(3, st);
-  // S4-S6 routed and shared SwiGLU experts, one launch per projection
-  moge::FfnSeg routed;
-  routed.x = x;
-  routed.row_src = sorted_pair;
-  routed.row_div = K;
-  routed.offsets = offsets;
-  routed.rows = R;
-  routed.n_exp = N;
-  routed.inter = dims->inter;
-  routed.w_gate = w_gate;
-  routed.w_up = w_up;
-  routed.w_down = w_down;
-  routed.h = at<char>(ws, p.h);
-  routed.y = at<char>(ws, p.y_perm);
-  moge::FfnSeg sh;
+size_t moge_packed_weights_size(const moge_dims_t* dims) {
+  const std::string saved = g_last_error;
+  const moge_status_t s = check_dims(dims);
+  g_last_error = saved;
+  if (s != MOGE_OK) return 0;
+  return moge::packed_parts(dims->d, dims->N, dims->inter, dims->shared_inter, esize(dims)).total;
+}
+
+moge_status_t moge_pack_weights(const moge_dims_t* dims, const void* w_gate, const void* w_up,
+                                const void* w_down, const void* ws_gate, const void* ws_up,
+                                const void* ws_down, void* packed, size_t packed_bytes,
+                                void* stream) {
+  CHECK(check_dims(dims));
+  const bool shared = dims->shared_inter > 0;
+  CHECK(check_ptr(w_gate, 16, "w_gate", true));
+  CHECK(check_ptr(w_up, 16, "w_up", true));
+  CHECK(check_ptr(w_down, 16, "w_down", true));
+  CHECK(check_ptr(ws_gate, 16, "ws_gate", shared));
+  CHECK(check_ptr(ws_up, 16, "ws_up", shared));
+  CHECK(check_ptr(ws_down, 16, "ws_down", shared));
+  CHECK(check_ptr(packed, 256, "packed", true));
+  const moge::PackedParts pp =
+      moge::packed_parts(dims->d, dims->N, dims->inter, dims->shared_inter, esize(dims));
+  if (packed_bytes < pp.total)
+    return fail(MOGE_ERR_INVALID_ARG, "packed buffer has %zu bytes, need %zu", packed_bytes,
+                pp.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* dst = static_cast<char*>(packed);
+  const int dt = dims->dtype, d = dims->d, N = dims->N, I = dims->inter, Is = dims->shared_inter;
+  CHECK(hip_check(moge::launch_pack(dt, w_gate, w_up, N, I, d, dst + pp.routed_gu, st),
+                  "pack routed gate/up"));
+  CHECK(hip_check(moge::launch_pack(dt, w_down, nullptr, N, d, I, dst + pp.routed_down, st),
+                  "pack routed down"));
   if (shared) {
-    sh.x = x;
-    sh.rows = T;
-    sh.n_exp = 1;
-    sh.inter = dims->shared_inter;
-    sh.w_gate = ws_gate;
-    sh.w_up = ws_up;
-    sh.w_down = ws_down;
-    sh.h = at<char>(ws, p.hs);
-    sh.y = at<char>(ws, p.sh);
+    CHECK(hip_check(moge::launch_pack(dt, ws_gate, ws_up, 1, Is, d, dst + pp.shared_gu, st),
+                    "pack shared gate/up"));
+    CHECK(hip_check(moge::launch_pack(dt, ws_down, nullptr, 1, d, Is, dst + pp.shared_down, st),
+                    "pack shared down"));
   }
-  CHECK(hip_check(moge::launch_ffn_gateup(dims->dtype, dims->d, routed, shared ? &sh : nullptr, st),
-                  "expert gate/up"));
-  mark(4, st);
-  CHECK(hip_check(moge::launch_ffn_down(dims->dtype, dims->d, routed, shared ? &sh : nullptr, st),
-                  "expert down"));
-  mark(5, st);
-  // S7 combine
-  CHECK(hip_check(moge::launch_combine(dims->dtype, T, K, dims->d, routed.y, pair_row, gate,
-                                       shared ? sh.y : nullptr, y, st),
-                  "combine"));
-  mark(6, st);
   return ok();
+}
+
+moge_status_t moge_layer_forward_packed(const moge_dims_t* dims, const void* x,
+                                        const void* w_router, const float* router_bias,
+                                        const void* packed, const float* logits_in, void* y,
+                                        float* logits_out, int32_t* topk_idx_out,
+                                        float* topk_gate_out, int32_t* group_counts_out,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_dims(dims));
+  CHECK(check_ptr(packed, 256, "packed", true));
+  const moge::PackedParts pp =
+      moge::packed_parts(dims->d, dims->N, dims->inter, dims->shared_inter, esize(dims));
+  const char* base = static_cast<const char*>(packed);
+  Weights w;
+  w.p_gu = base + pp.routed_gu;
+  w.p_down = base + pp.routed_down;
+  if (dims->shared_inter > 0) {
+    w.ps_gu = base + pp.shared_gu;
+    w.ps_down = base + pp.shared_down;
+  }
+  return layer_impl(dims, x, w_router, router_bias, w, logits_in, y, logits_out, topk_idx_out,
+                    topk_gate_out, group_counts_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -37,33 +37,51 @@ template <> struct Vec8Io<float> {
   }
 };
 
+// grid (T, ceil(d / 512)); thread = 8 consecutive features of one token.  The
+// slot loop is unrolled by 8 so the K row loads of a token are in flight together;
+// the additions still run in slot order.
 template <typename E>
-__global__ __launch_bounds__(256) void k_combine(int T, int K, int d, int R,
-                                                 const E* __restrict__ y_perm,
-                                                 const int32_t* __restrict__ pair_row,
-                                                 const float* __restrict__ gate,
-                                                 const E* __restrict__ shared, E* __restrict__ y) {
+__global__ __launch_bounds__(64) void k_combine(int T, int K, int d, int R,
+                                                const E* __restrict__ y_perm,
+                                                const int32_t* __restrict__ pair_row,
+                                                const float* __restrict__ gate,
+                                                const E* __restrict__ shared, E* __restrict__ y) {
   const int t = blockIdx.x;
-  const int nvec = d / 8;
-  for (int c = threadIdx.x; c < nvec; c += blockDim.x) {
-    float acc[8];
-    if (shared) {
-      Vec8Io<E>::load(shared + (size_t)t * d + c * 8, acc);
-    } else {
+  const int c = blockIdx.y * 64 + threadIdx.x;
+  if (c >= d / 8) return;
+  float acc[8];
+  if (shared) {
+    Vec8Io<E>::load(shared + (size_t)t * d + c * 8, acc);
+  } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    }
-    for (int k = 0; k < K; ++k) {
-      const int row = pair_row[(size_t)t * K + k];
-      if (row < 0 || row >= R) continue;
-      const float g = gate[(size_t)t * K + k];
-      float v[8];
-      Vec8Io<E>::load(y_perm + (size_t)row * d + c * 8, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
-    }
-    Vec8Io<E>::store(y + (size_t)t * d + c * 8, acc);
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   }
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    int rows[8];
+    float g[8], v[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + j;
+      rows[j] = k < K ? pair_row[(size_t)t * K + k] : -1;
+      g[j] = k < K ? gate[(size_t)t * K + k] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (rows[j] >= 0 && rows[j] < R) {
+        Vec8Io<E>::load(y_perm + (size_t)rows[j] * d + c * 8, v[j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < K && rows[j] >= 0 && rows[j] < R) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], v[j][i], acc[i]);
+      }
+  }
+  Vec8Io<E>::store(y + (size_t)t * d + c * 8, acc);
 }
 
 hipError_t launch_combine(int dtype, int T, int K, int d, const void* y_perm,
@@ -71,13 +89,13 @@ hipError_t launch_combine(int dtype, int T, int K, int d, const void* y_perm,
                           void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int R = T * K;
-  const int threads = (d / 8) >= 256 ? 256 : 64;
+  dim3 grid(T, (d / 8 + 63) / 64);
   if (dtype == 1)
-    hipLaunchKernelGGL(k_combine<bf16>, dim3(T), dim3(threads), 0, st, T, K, d, R,
-                       (const bf16*)y_perm, pair_row, gate, (const bf16*)shared, (bf16*)y);
+    hipLaunchKernelGGL(k_combine<bf16>, grid, dim3(64), 0, st, T, K, d, R, (const bf16*)y_perm,
+                       pair_row, gate, (const bf16*)shared, (bf16*)y);
   else
-    hipLaunchKernelGGL(k_combine<float>, dim3(T), dim3(threads), 0, st, T, K, d, R,
-                       (const float*)y_perm, pair_row, gate, (const float*)shared, (float*)y);
+    hipLaunchKernelGGL(k_combine<float>, grid, dim3(64), 0, st, T, K, d, R, (const float*)y_perm,
+                       pair_row, gate, (const float*)shared, (float*)y);
   return hipGetLastError();
 }
 

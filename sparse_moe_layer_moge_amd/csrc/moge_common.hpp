@@ -17,6 +17,24 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
+// Buffer resources: a base address and a byte range held in scalar registers.
+// A buffer load takes a 32-bit per-lane offset plus a wave-uniform scalar offset,
+// so a streaming loop needs no 64-bit address registers per in-flight load, and
+// loads outside the range return zeros instead of faulting.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBufferConfigGfx9 = 0x00020000;  // raw (untyped) buffer, gfx9 family
+constexpr int kLoadNonTemporal = 2;            // cache-policy bit: streamed once
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
+                                           kBufferConfigGfx9);
+}
+
+// ---------------------------------------------------------------------------
 // Eight consecutive elements along the contraction dimension: the per-lane share
 // of one K=32 step of a 16x16 MFMA tile.  bf16: 16 bytes, one v_mfma 16x16x32.
 // float: 32 bytes, eight v_mfma 16x16x4 (element j of every lane feeds the j-th
@@ -27,6 +45,10 @@ template <typename E> struct Frag8;
 
 template <> struct Frag8<bf16> {
   u32x4 v;
+  template <int AUX>
+  __device__ __forceinline__ void load_buf(Rsrc r, uint32_t voff, uint32_t soff) {
+    v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+  }
   __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const u32x4*>(p); }
   __device__ __forceinline__ void load_nt(const bf16* p) {
     v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -36,6 +58,11 @@ template <> struct Frag8<bf16> {
 
 template <> struct Frag8<float> {
   f32x4 lo, hi;
+  template <int AUX>
+  __device__ __forceinline__ void load_buf(Rsrc r, uint32_t voff, uint32_t soff) {
+    lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+    hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, AUX));
+  }
   __device__ __forceinline__ void load(const float* p) {
     lo = *reinterpret_cast<const f32x4*>(p);
     hi = *reinterpret_cast<const f32x4*>(p + 4);

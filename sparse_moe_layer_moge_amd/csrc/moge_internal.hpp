@@ -32,19 +32,22 @@ hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* sorted_pa
 // ---- expert FFN (ffn.hip) --------------------------------------------------
 // One segment = a set of SwiGLU experts sharing a weight layout.  Row r of the
 // segment reads activation row x[row_src ? row_src[r] / row_div : r].  Expert e
-// owns rows offsets[e] .. offsets[e+1]; offsets == nullptr means a single expert
-// owning rows [0, rows).
+// owns rows offsets[e] .. offsets[e+1] (clamped into [0, rows]); offsets ==
+// nullptr means a single expert owning rows [0, rows).  h and y hold `rows` rows.
 struct FfnSeg {
   const void* x = nullptr;
+  int x_rows = 0;                // rows of x (bounds of the activation buffer)
   const int32_t* row_src = nullptr;
   int row_div = 1;
   const int32_t* offsets = nullptr;
   int rows = 0;
   int n_exp = 0;
   int inter = 0;
-  const void* w_gate = nullptr;  // [n_exp, inter, d]
+  const void* w_gate = nullptr;  // [n_exp, inter, d]  row-major weights, or
   const void* w_up = nullptr;    // [n_exp, inter, d]
   const void* w_down = nullptr;  // [n_exp, d, inter]
+  const void* p_gu = nullptr;    // packed gate/up parts, expert-strided (packed_layout.hpp)
+  const void* p_down = nullptr;  // packed down parts, expert-strided
   void* h = nullptr;             // [rows, inter] dtype (gate/up output, down input)
   void* y = nullptr;             // [rows, d] dtype
 };
@@ -52,6 +55,11 @@ struct FfnSeg {
 hipError_t launch_ffn_gateup(int dtype, int d, const FfnSeg& a, const FfnSeg* b, hipStream_t st);
 // down projection for up to two segments in one launch
 hipError_t launch_ffn_down(int dtype, int d, const FfnSeg& a, const FfnSeg* b, hipStream_t st);
+
+// ---- weight packing (pack.hip) --------------------------------------------
+// src1 != nullptr: gate/up pair [n_exp, rows, K] each; else down [n_exp, rows, K]
+hipError_t launch_pack(int dtype, const void* src0, const void* src1, int n_exp, int rows, int K,
+                       void* dst, hipStream_t st);
 
 // ---- combine (combine.hip) -------------------------------------------------
 hipError_t launch_combine(int dtype, int T, int K, int d, const void* y_perm,

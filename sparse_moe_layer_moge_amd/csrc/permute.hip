@@ -1,19 +1,25 @@
 // Permutation of the (token, slot) pairs into expert-contiguous order.
 //
 // Rows are sorted by expert, then by token, so the result is unique and the
-// kernels below reproduce it bit for bit without ordered atomics:
-//   1. k_block_hist: per 64-token block, how many pairs go to each expert
-//      (popcounts of wave ballots; integer counts, no atomics);
-//   2. k_scan: per expert, exclusive prefix over blocks, then over experts ->
-//      counts, offsets, per-group loads (every group load equals T*K', the zero
+// kernels below reproduce it bit for bit without ordered atomics.  Tokens are
+// handled in chunks of 64, one token per lane:
+//   1. per chunk and expert, how many of the chunk's tokens chose the expert
+//      (popcount of a wave ballot);
+//   2. per expert, an exclusive prefix over chunks, then over experts -> counts,
+//      offsets and per-group loads (every group load equals T*K', the zero
 //      imbalance the grouped routing guarantees: TechWalker page, section 一);
-//   3. k_scatter: inside a block, the rank of a token among the block's tokens
-//      that chose the same expert is a popcount of a wave ballot, so rows come
-//      out in token order.
+//   3. per chunk, the ballot masks again; the rank of a token among the chunk's
+//      tokens that chose expert e is popcount(mask_e & lanes-below-me), so rows
+//      come out in token order.
+// Up to kSmallChunks chunks run in one workgroup (one launch, all counts in LDS);
+// larger batches use a three-kernel version with the same arithmetic.
 #include "moge_common.hpp"
 #include "moge_internal.hpp"
 
 namespace moge {
+
+constexpr int kSmallWaves = 16;    // waves of the single-workgroup kernel
+constexpr int kSmallChunks = 64;   // chunks it handles (T <= 4096)
 
 // The set of experts token t chose (entries outside [0, N) and repeats ignored;
 // moge_route never produces either).
@@ -27,16 +33,122 @@ __device__ __forceinline__ void chosen_set(const int32_t* __restrict__ idx, int 
   }
 }
 
-__global__ __launch_bounds__(kPermTokens) void k_block_hist(const int32_t* __restrict__ idx,
-                                                            int T, int K, int N,
-                                                            int32_t* __restrict__ blk_cnt) {
+__device__ __forceinline__ bool in_set(const uint64_t (&s)[4], int e) {
+  return (s[e >> 6] >> (e & 63)) & 1ull;
+}
+
+// per-expert ballot masks of one chunk (lane 0 writes them)
+__device__ __forceinline__ void chunk_masks(const uint64_t (&chosen)[4], int N,
+                                            uint64_t* __restrict__ masks) {
+  const int l = threadIdx.x & 63;
+  for (int e = 0; e < N; ++e) {
+    const uint64_t m = __ballot(in_set(chosen, e));
+    if (l == 0) masks[e] = m;
+  }
+}
+
+// rows of one chunk's pairs: row = offsets[e] + base[e] + rank in chunk; slots
+// without a row (invalid or repeated expert) get pair_row = -1
+__device__ __forceinline__ void chunk_scatter(const int32_t* __restrict__ idx, int t, int K,
+                                              int N, bool valid, const int32_t* offsets,
+                                              const int32_t* base, const uint64_t* masks,
+                                              int32_t* __restrict__ sorted_pair,
+                                              int32_t* __restrict__ pair_row) {
+  if (!valid) return;
+  const uint64_t lt = lanemask_lt();
+  uint64_t seen[4] = {0ull, 0ull, 0ull, 0ull};
+  for (int k = 0; k < K; ++k) {
+    const int e = idx[(size_t)t * K + k];
+    int row = -1;
+    if ((unsigned)e < (unsigned)N && !in_set(seen, e)) {
+      seen[e >> 6] |= 1ull << (e & 63);
+      row = offsets[e] + base[e] + __popcll(masks[e] & lt);
+      sorted_pair[row] = t * K + k;
+    }
+    pair_row[(size_t)t * K + k] = row;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// single workgroup: T <= 64 * kSmallChunks
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * kSmallWaves) void k_permute_small(
+    const int32_t* __restrict__ idx, int T, int K, int N, int M, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ group_counts,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row) {
+  __shared__ int32_t s_base[kSmallChunks][256];     // counts, then prefix over chunks
+  __shared__ uint64_t s_mask[kSmallWaves][256];
+  __shared__ int32_t s_cnt[256];
+  __shared__ int32_t s_off[257];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int nchunks = (T + 63) / 64;
+
+  for (int c = w; c < nchunks; c += kSmallWaves) {
+    const int t = c * 64 + l;
+    uint64_t chosen[4];
+    chosen_set(idx, t, K, N, t < T, chosen);
+    for (int e = 0; e < N; ++e) {
+      const uint64_t m = __ballot(in_set(chosen, e));
+      if (l == 0) s_base[c][e] = __popcll(m);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = s_base[c][e];
+      s_base[c][e] = run;
+      run += v;
+    }
+    s_cnt[e] = run;
+    counts[e] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int e = 0; e < N; ++e) {
+      s_off[e] = acc;
+      offsets[e] = acc;
+      acc += s_cnt[e];
+    }
+    s_off[N] = acc;
+    offsets[N] = acc;
+  }
+  const int G = N / M;
+  for (int g = threadIdx.x; g < M; g += blockDim.x) {
+    int sum = 0;
+    for (int q = 0; q < G; ++q) sum += s_cnt[g * G + q];
+    group_counts[g] = sum;
+  }
+  __syncthreads();
+  for (int c = w; c < nchunks; c += kSmallWaves) {
+    const int t = c * 64 + l;
+    uint64_t chosen[4];
+    chosen_set(idx, t, K, N, t < T, chosen);
+    chunk_masks(chosen, N, s_mask[w]);
+    // lane 0's mask stores must be visible to the whole wave before the reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    chunk_scatter(idx, t, K, N, t < T, s_off, s_base[c], s_mask[w], sorted_pair, pair_row);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// ---------------------------------------------------------------------------
+// large batches: one wave per chunk, three launches
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_chunk_hist(const int32_t* __restrict__ idx, int T, int K,
+                                                   int N, int32_t* __restrict__ blk_cnt) {
   const int l = threadIdx.x;
-  const int t = blockIdx.x * kPermTokens + l;
+  const int t = blockIdx.x * 64 + l;
   uint64_t chosen[4];
   chosen_set(idx, t, K, N, t < T, chosen);
   int32_t* out = blk_cnt + (size_t)blockIdx.x * N;
   for (int e = 0; e < N; ++e) {
-    const uint64_t m = __ballot((chosen[e >> 6] >> (e & 63)) & 1ull);
+    const uint64_t m = __ballot(in_set(chosen, e));
     if (l == 0) out[e] = __popcll(m);
   }
 }
@@ -74,34 +186,26 @@ __global__ __launch_bounds__(256) void k_scan(const int32_t* __restrict__ blk_cn
   }
 }
 
-__global__ __launch_bounds__(kPermTokens) void k_scatter(const int32_t* __restrict__ idx, int T,
-                                                         int K, int N,
-                                                         const int32_t* __restrict__ offsets,
-                                                         const int32_t* __restrict__ blk_base,
-                                                         int32_t* __restrict__ sorted_pair,
-                                                         int32_t* __restrict__ pair_row) {
+__global__ __launch_bounds__(64) void k_chunk_scatter(const int32_t* __restrict__ idx, int T,
+                                                      int K, int N,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ blk_base,
+                                                      int32_t* __restrict__ sorted_pair,
+                                                      int32_t* __restrict__ pair_row) {
+  __shared__ uint64_t s_mask[256];
+  __shared__ int32_t s_off[256];
+  __shared__ int32_t s_base[256];
   const int l = threadIdx.x;
-  const int t = blockIdx.x * kPermTokens + l;
-  const bool valid = t < T;
-  uint64_t chosen[4];
-  chosen_set(idx, t, K, N, valid, chosen);
-  // slots that get no row (invalid or repeated expert) keep pair_row = -1
-  if (valid)
-    for (int k = 0; k < K; ++k) pair_row[(size_t)t * K + k] = -1;
-  const uint64_t lt = lanemask_lt();
-  const int32_t* base = blk_base + (size_t)blockIdx.x * N;
-  for (int e = 0; e < N; ++e) {
-    const bool has = (chosen[e >> 6] >> (e & 63)) & 1ull;
-    const uint64_t m = __ballot(has);
-    if (m == 0ull) continue;
-    if (has) {
-      int slot = 0;
-      while (idx[(size_t)t * K + slot] != e) ++slot;
-      const int row = offsets[e] + base[e] + __popcll(m & lt);
-      sorted_pair[row] = t * K + slot;
-      pair_row[(size_t)t * K + slot] = row;
-    }
+  const int t = blockIdx.x * 64 + l;
+  for (int e = l; e < N; e += 64) {
+    s_off[e] = offsets[e];
+    s_base[e] = blk_base[(size_t)blockIdx.x * N + e];
   }
+  uint64_t chosen[4];
+  chosen_set(idx, t, K, N, t < T, chosen);
+  chunk_masks(chosen, N, s_mask);
+  __syncthreads();
+  chunk_scatter(idx, t, K, N, t < T, s_off, s_base, s_mask, sorted_pair, pair_row);
 }
 
 hipError_t launch_permute(const int32_t* idx, int T, int K, int N, int M, int32_t* blk_cnt,
@@ -109,10 +213,15 @@ hipError_t launch_permute(const int32_t* idx, int T, int K, int N, int M, int32_
                           int32_t* group_counts, int32_t* sorted_pair, int32_t* pair_row,
                           hipStream_t st) {
   const int nblk = perm_blocks(T);
-  hipLaunchKernelGGL(k_block_hist, dim3(nblk), dim3(kPermTokens), 0, st, idx, T, K, N, blk_cnt);
+  if (nblk <= kSmallChunks) {
+    hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(64 * kSmallWaves), 0, st, idx, T, K, N, M,
+                       counts, offsets, group_counts, sorted_pair, pair_row);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_chunk_hist, dim3(nblk), dim3(64), 0, st, idx, T, K, N, blk_cnt);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, st, blk_cnt, nblk, N, M, counts, offsets,
                      group_counts, blk_base);
-  hipLaunchKernelGGL(k_scatter, dim3(nblk), dim3(kPermTokens), 0, st, idx, T, K, N, offsets,
+  hipLaunchKernelGGL(k_chunk_scatter, dim3(nblk), dim3(64), 0, st, idx, T, K, N, offsets,
                      blk_base, sorted_pair, pair_row);
   return hipGetLastError();
 }

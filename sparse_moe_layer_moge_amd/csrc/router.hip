@@ -8,6 +8,7 @@
 // groups is zero.
 #include "moge_common.hpp"
 #include "moge_internal.hpp"
+#include "stream_tile.hpp"
 
 namespace moge {
 
@@ -18,7 +19,7 @@ namespace moge {
 // Splitting the contraction gives the small-T (decode) case enough waves; the
 // partial sums are added in a fixed order by the routing kernel.
 // ---------------------------------------------------------------------------
-template <typename E>
+template <typename E, int PW>
 __global__ __launch_bounds__(64) void k_router_scores(const E* __restrict__ x,
                                                       const E* __restrict__ wr, int T, int d,
                                                       int N, int steps_per_split,
@@ -27,36 +28,40 @@ __global__ __launch_bounds__(64) void k_router_scores(const E* __restrict__ x,
   const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16, ks = blockIdx.z;
   const int nsteps = d / 32;
   const int s0 = ks * steps_per_split;
-  const int s1 = min(nsteps, s0 + steps_per_split);
-  const int ln = l & 15, kq = (l >> 4) * 8;
-  const E* pa = wr + (size_t)min(e0 + ln, N - 1) * d + kq;
-  const E* pb = x + (size_t)min(t0 + ln, T - 1) * d + kq;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = s0; s < s1; ++s) {
-    Frag8<E> a, b;
-    a.load(pa + s * 32);
-    b.load(pb + s * 32);
-    acc = mfma_step(a, b, acc);
+  const int n = min(nsteps, s0 + steps_per_split) - s0;
+  f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
+  if (n > 0) {
+    const int ln = l & 15, kq = (l >> 4) * 8;
+    const uint32_t base = (uint32_t)((s0 * 32 + kq) * sizeof(E));
+    const Rsrc rw[1] = {make_rsrc(wr, (uint64_t)N * d * sizeof(E))};
+    const uint32_t vw[1] = {(uint32_t)(min(e0 + ln, N - 1) * d * sizeof(E)) + base};
+    const uint32_t vx[1] = {(uint32_t)((size_t)min(t0 + ln, T - 1) * d * sizeof(E)) + base};
+    const Rsrc rx = make_rsrc(x, (uint64_t)T * d * sizeof(E));
+    if (n >= PW)
+      stream_tile<E, 1, 1, PW>(rw, vw, 32 * sizeof(E), rx, vx, n, 0, acc);
+    else
+      stream_tile<E, 1, 1, 1>(rw, vw, 32 * sizeof(E), rx, vx, n, 0, acc);
   }
-  const int t = t0 + ln;
+  const int t = t0 + (l & 15);
   if (t < T) {
     float* out = partial + ((size_t)ks * T + t) * N;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = e0 + 4 * (l >> 4) + i;
-      if (e < N) out[e] = acc[i];
+      if (e < N) out[e] = acc[0][0][i];
     }
   }
 }
 
 int router_ksplit(int T, int d, int N) {
+  // enough waves to spread the router weight and x over the CUs at decode sizes,
+  // few partial sums at prefill sizes
   const int tiles = ((T + 15) / 16) * ((N + 15) / 16);
   const int nsteps = d / 32;
-  int ks = 2048 / (tiles > 0 ? tiles : 1);
+  int ks = 512 / (tiles > 0 ? tiles : 1);
   if (ks < 1) ks = 1;
+  if (ks > 16) ks = 16;
   if (ks > nsteps) ks = nsteps;
-  if (ks > 64) ks = 64;
   return ks;
 }
 
@@ -66,10 +71,10 @@ hipError_t launch_router_scores(int dtype, const void* x, const void* w_router, 
   const int per = (nsteps + ksplit - 1) / ksplit;
   dim3 grid((N + 15) / 16, (T + 15) / 16, ksplit);
   if (dtype == 1)
-    hipLaunchKernelGGL(k_router_scores<bf16>, grid, dim3(64), 0, st, (const bf16*)x,
+    hipLaunchKernelGGL((k_router_scores<bf16, 4>), grid, dim3(64), 0, st, (const bf16*)x,
                        (const bf16*)w_router, T, d, N, per, partial);
   else
-    hipLaunchKernelGGL(k_router_scores<float>, grid, dim3(64), 0, st, (const float*)x,
+    hipLaunchKernelGGL((k_router_scores<float, 4>), grid, dim3(64), 0, st, (const float*)x,
                        (const float*)w_router, T, d, N, per, partial);
   return hipGetLastError();
 }
@@ -103,8 +108,10 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ partial
     const int e = l + 64 * j;
     v[j] = -INFINITY;
     if (e < N) {
-      // start from split 0 (not from 0.f) so a lone -0.0 score keeps its sign
+      // start from split 0 (not from 0.f) so a lone -0.0 score keeps its sign;
+      // splits are added in increasing order (loads batched by the unroll)
       float s = partial[(size_t)tt * N + e];
+#pragma unroll 8
       for (int ks = 1; ks < ksplit; ++ks) s += partial[((size_t)ks * T + tt) * N + e];
       if (bias) s += bias[e];
       v[j] = s;
