@@ -48,6 +48,7 @@ struct FfnSeg {
   const void* w_down = nullptr;  // [n_exp, d, inter]
   const void* p_gu = nullptr;    // packed gate/up parts, expert-strided (packed_layout.hpp)
   const void* p_down = nullptr;  // packed down parts, expert-strided
+  int nblk = 1;                  // row blocks per wave (set by the launcher)
   void* h = nullptr;             // [rows, inter] dtype (gate/up output, down input)
   void* y = nullptr;             // [rows, d] dtype
 };

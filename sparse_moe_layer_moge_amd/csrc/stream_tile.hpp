@@ -68,6 +68,80 @@ __device__ __forceinline__ void stream_tile(const Rsrc (&wr)[NB], const uint32_t
     if (s + PW + p < nsteps) compute(p);
 }
 
+// stream_blocks: the same stream over `nblk` consecutive row blocks that share
+// the activation rows (the next block's weights start blk_bytes further on; in
+// the packed layout that is the very next byte).  The ring runs on across block
+// boundaries, so a wave never drains its loads between blocks; after the last
+// step of block b, flush(b, acc) consumes the block's sums and acc restarts at 0.
+// Needs nblk * nsteps >= PW.
+template <typename E, int NB, int MS, int PW, typename Flush>
+__device__ __forceinline__ void stream_blocks(const Rsrc (&wr)[NB], const uint32_t (&wv)[NB],
+                                              uint32_t wstep, uint32_t blk_bytes, Rsrc xr,
+                                              const uint32_t (&xv)[MS], int nsteps, int nblk,
+                                              int s0, Flush&& flush) {
+  constexpr uint32_t kStepBytes = 32 * sizeof(E);
+  Frag8<E> wb[PW][NB];
+  Frag8<E> xb[PW][MS];
+  f32x4 acc[NB][MS];
+  auto zero = [&]() {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) acc[nb][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // load side: block, rotated step index, steps done in the block (wave-uniform)
+  int l_blk = 0, l_j = s0, l_cnt = 0;
+  auto load = [&](int slot) {
+    const uint32_t wso = (uint32_t)l_blk * blk_bytes + (uint32_t)l_j * wstep;
+    const uint32_t xso = (uint32_t)l_j * kStepBytes;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) wb[slot][nb].template load_buf<kLoadNonTemporal>(wr[nb], wv[nb], wso);
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) xb[slot][ms].template load_buf<0>(xr, xv[ms], xso);
+    l_j = (l_j + 1 == nsteps) ? 0 : l_j + 1;
+    if (++l_cnt == nsteps) {
+      l_cnt = 0;
+      ++l_blk;
+    }
+  };
+  // compute side
+  int c_blk = 0, c_cnt = 0;
+  auto compute = [&](int slot) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) acc[nb][ms] = mfma_step(wb[slot][nb], xb[slot][ms], acc[nb][ms]);
+    if (++c_cnt == nsteps) {
+      flush(c_blk, acc);
+      zero();
+      c_cnt = 0;
+      ++c_blk;
+    }
+  };
+
+  zero();
+  const int total = nsteps * nblk;
+#pragma unroll
+  for (int p = 0; p < PW; ++p) load(p);
+  int q = 0;
+  for (; q + 2 * PW <= total; q += PW) {
+#pragma unroll
+    for (int p = 0; p < PW; ++p) {
+      compute(p);
+      load(p);
+    }
+  }
+  // slots hold steps q .. q+PW-1; total - q is in [PW, 2*PW)
+#pragma unroll
+  for (int p = 0; p < PW; ++p) {
+    compute(p);
+    if (q + PW + p < total) load(p);
+  }
+#pragma unroll
+  for (int p = 0; p < PW; ++p)
+    if (q + PW + p < total) compute(p);
+}
+
 // Prefetch depth by row-subtile count: deep for the decode case (MS = 1), less
 // when the activation fragments and accumulators take more registers, so every
 // bf16 variant fits 3 waves per SIMD; float fragments are twice as wide.
