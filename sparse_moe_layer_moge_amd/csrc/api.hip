@@ -1,6 +1,7 @@
 // C ABI of the MoGE layer library: host-side validation, workspace carving and
 // kernel dispatch on the caller's stream.  No device allocation, no host
 // synchronisation, no host reads of device data.
+#include <limits.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -153,6 +154,69 @@ moge_status_t check_ws(const moge_dims_t* d, void* ws, size_t ws_bytes, Plan* pl
   return MOGE_OK;
 }
 
+// The tile-path view of a streaming segment: gate/up reads x (or x_perm) and
+// writes H; down reads H and writes y.
+moge::TileSeg tile_view(const moge::FfnSeg& f, bool gateup) {
+  moge::TileSeg t;
+  t.n_exp = f.n_exp;
+  t.inter = f.inter;
+  t.thr = f.thr;
+  t.offsets = f.offsets;
+  t.rows = f.rows;
+  if (gateup) {
+    t.x = f.x;
+    t.x_rows = f.x_rows;
+    t.row_src = f.row_src;
+    t.row_div = f.row_div;
+    t.w0 = f.w_gate;
+    t.w1 = f.w_up;
+    t.packed = f.p_gu;
+    t.out = f.h;
+  } else {
+    t.x = f.h;
+    t.x_rows = f.rows;
+    t.w0 = f.w_down;
+    t.packed = f.p_down;
+    t.out = f.y;
+  }
+  return t;
+}
+
+// Both projections of up to two segments: the streaming kernels take experts with
+// at most `thr` rows, the tile kernels the others (launched only when some expert
+// can have more: an expert never has more rows than the batch has tokens).
+moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh,
+                      hipStream_t st, bool marks) {
+  // the tile path covers bf16 and its tile shapes; everything else streams
+  const bool tiles_ok = dtype == MOGE_BF16 && moge::tile_path_ok(d, routed.inter) &&
+                        (!sh || moge::tile_path_ok(d, sh->inter));
+  const int thr = tiles_ok ? moge::kStreamMaxRows : INT_MAX;
+  routed.thr = thr;
+  const bool big = T > thr;
+  const bool sh_tile = sh && sh->rows > thr;
+  if (sh) sh->thr = thr;
+  moge::FfnSeg* sh_stream = (sh && !sh_tile) ? sh : nullptr;
+  CHECK(hip_check(moge::launch_ffn_gateup(dtype, d, routed, sh_stream, st), "expert gate/up"));
+  if (big) {
+    const moge::TileSeg a = tile_view(routed, true);
+    moge::TileSeg b;
+    if (sh_tile) b = tile_view(*sh, true);
+    CHECK(hip_check(moge::launch_ffn_tile(true, d, a, sh_tile ? &b : nullptr, st),
+                    "expert gate/up tiles"));
+  }
+  if (marks) mark(4, st);
+  CHECK(hip_check(moge::launch_ffn_down(dtype, d, routed, sh_stream, st), "expert down"));
+  if (big) {
+    const moge::TileSeg a = tile_view(routed, false);
+    moge::TileSeg b;
+    if (sh_tile) b = tile_view(*sh, false);
+    CHECK(hip_check(moge::launch_ffn_tile(false, d, a, sh_tile ? &b : nullptr, st),
+                    "expert down tiles"));
+  }
+  if (marks) mark(5, st);
+  return MOGE_OK;
+}
+
 struct Weights {
   const void *gate = nullptr, *up = nullptr, *down = nullptr;        // row-major routed
   const void *s_gate = nullptr, *s_up = nullptr, *s_down = nullptr;  // row-major shared
@@ -247,12 +311,7 @@ moge_status_t layer_impl(const moge_dims_t* dims, const void* x, const void* w_r
     sh.h = at<char>(ws, p.hs);
     sh.y = at<char>(ws, p.sh);
   }
-  CHECK(hip_check(moge::launch_ffn_gateup(dims->dtype, dims->d, routed, shared ? &sh : nullptr, st),
-                  "expert gate/up"));
-  mark(4, st);
-  CHECK(hip_check(moge::launch_ffn_down(dims->dtype, dims->d, routed, shared ? &sh : nullptr, st),
-                  "expert down"));
-  mark(5, st);
+  CHECK(run_ffn(dims->dtype, dims->d, T, routed, shared ? &sh : nullptr, st, true));
   // S7 combine
   CHECK(hip_check(moge::launch_combine(dims->dtype, T, K, dims->d, routed.y, pair_row, gate,
                                        shared ? sh.y : nullptr, y, st),
@@ -364,10 +423,7 @@ moge_status_t moge_expert_ffn(const moge_dims_t* dims, const void* x_perm,
   g.w_down = w_down;
   g.h = at<char>(ws, p.h);
   g.y = y_perm;
-  CHECK(hip_check(moge::launch_ffn_gateup(dims->dtype, dims->d, g, nullptr, st),
-                  "moge_expert_ffn gate/up"));
-  CHECK(hip_check(moge::launch_ffn_down(dims->dtype, dims->d, g, nullptr, st),
-                  "moge_expert_ffn down"));
+  CHECK(run_ffn(dims->dtype, dims->d, dims->T, g, nullptr, st, false));
   return ok();
 }
 

@@ -37,6 +37,7 @@ __device__ __forceinline__ SegView expert_rows(const FfnSeg& g, int e) {
     v.lo = 0;
     v.cnt = g.rows;
   }
+  if (v.cnt > g.thr) v.cnt = 0;   // the tile path's expert
   return v;
 }
 

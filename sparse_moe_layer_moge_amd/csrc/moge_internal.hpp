@@ -49,6 +49,7 @@ struct FfnSeg {
   const void* p_gu = nullptr;    // packed gate/up parts, expert-strided (packed_layout.hpp)
   const void* p_down = nullptr;  // packed down parts, expert-strided
   int nblk = 1;                  // row blocks per wave (set by the launcher)
+  int thr = 0x7fffffff;          // experts with more rows than this are left to the tile path
   void* h = nullptr;             // [rows, inter] dtype (gate/up output, down input)
   void* y = nullptr;             // [rows, d] dtype
 };
@@ -56,6 +57,28 @@ struct FfnSeg {
 hipError_t launch_ffn_gateup(int dtype, int d, const FfnSeg& a, const FfnSeg* b, hipStream_t st);
 // down projection for up to two segments in one launch
 hipError_t launch_ffn_down(int dtype, int d, const FfnSeg& a, const FfnSeg* b, hipStream_t st);
+
+// ---- expert FFN, MFMA tile path (tile_gemm.hip, bf16) ----------------------
+// Experts with more than `thr` rows: 128-row x 128-weight-row tiles through LDS.
+constexpr int kStreamMaxRows = 64;  // the streaming path's row limit (4 row subtiles)
+struct TileSeg {
+  const void* x = nullptr;         // activation rows (x, or H for the down projection)
+  int x_rows = 0;
+  const int32_t* row_src = nullptr;
+  int row_div = 1;
+  const int32_t* offsets = nullptr;  // nullptr: one expert with `rows` rows
+  int rows = 0;
+  int n_exp = 0;
+  int inter = 0;
+  int thr = 0;                     // experts with more rows than this take the tile path
+  const void* w0 = nullptr;        // row-major: gate (gate/up) or down
+  const void* w1 = nullptr;        // row-major: up (gate/up)
+  const void* packed = nullptr;    // packed part (expert-strided), or nullptr
+  void* out = nullptr;             // H (gate/up) or y (down)
+};
+hipError_t launch_ffn_tile(bool gateup, int d, const TileSeg& a, const TileSeg* b, hipStream_t st);
+// shapes the tile kernels cover (96-feature gate/up tiles, 256-column down tiles)
+bool tile_path_ok(int d, int inter);
 
 // ---- weight packing (pack.hip) --------------------------------------------
 // src1 != nullptr: gate/up pair [n_exp, rows, K] each; else down [n_exp, rows, K]
