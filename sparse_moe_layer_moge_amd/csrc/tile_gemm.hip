@@ -7,16 +7,21 @@
 //   gate/up: 96 intermediate features (their 96 gate and 96 up weight rows), SwiGLU
 //            in the epilogue, H rounded once;
 //   down:    256 output columns.
-// Every wave owns 128 rows x (96 | 128) weight rows, i.e. 8 row fragments x (6 | 8)
-// weight fragments of 16x16 accumulators, which keeps the LDS bytes read per MFMA
-// and the global bytes per flop low enough to feed the matrix cores.
+// Every wave owns 128 rows x (96 | 128) weight rows as 4 x (3 | 4) blocks of 32x32
+// float32 accumulators (v_mfma_f32_32x32x16_bf16).
 //
-// The contraction runs in stages of 32 through kStages LDS buffers.  Operands go
-// from global memory straight into LDS (buffer loads with the LDS destination, one
-// 16-row x 32-element MFMA fragment = 1 KiB per wave instruction, so LDS holds
-// both operands in fragment order and every fragment read is 64 contiguous lanes
-// of 16 bytes), issued kStages-1 stages ahead of their use; a stage boundary is a
-// counted wait for the wave's own loads of that stage plus a workgroup barrier.
+// The contraction runs in stages of 64 elements through two LDS buffers, filled
+// straight from global memory (buffer loads with the LDS destination).  What makes
+// these loads fast is that every 16-lane quarter of a wave instruction reads whole
+// 128-byte lines:
+//   A (activation rows): 8 rows x 128 bytes per instruction, each row's line stored
+//     with its eight 16-byte chunks XOR-swizzled by the row index (chunk c of row r
+//     at position c ^ ((r >> 1) & 7)), so the MFMA operand reads are free of bank
+//     conflicts;
+//   B (weight rows): in MFMA fragment order, one 16-row x 32-element fragment (1 KiB,
+//     contiguous in the packed weight layout) per instruction.
+// The loads of stage k + 1 are spread between the MFMAs of stage k; a stage
+// boundary is a wait for the wave's own loads plus a workgroup barrier.
 //
 // The tiles of all experts form one list: for every expert above the threshold
 // ceil(rows / 256) row tiles, each paired with every weight tile; the shared
@@ -25,6 +30,8 @@
 // and go to the same XCD, so an activation tile is read from one L2.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "moge_common.hpp"
 #include "moge_internal.hpp"
 #include "packed_layout.hpp"
@@ -32,40 +39,36 @@
 namespace moge {
 
 constexpr int kTileM = 256;        // rows per tile
-constexpr int kTileK = 32;         // contraction elements per stage (one MFMA step)
-constexpr int kStages = 4;         // LDS buffers; loads run kStages-1 stages ahead
+constexpr int kTileK = 64;         // contraction elements per stage
+constexpr int kLineBytes = kTileK * 2;  // one operand row of a stage (bf16)
+constexpr int kStages = 2;         // LDS buffers
 constexpr int kTileThreads = 256;  // 4 waves: 2 (rows) x 2 (weight rows)
 constexpr int kXcds = 8;
-constexpr int kFragBytes = 1024;   // one bf16 fragment: 64 lanes x 16 bytes
-constexpr int kAFrags = kTileM / 16;                   // 16 row fragments per stage
-constexpr int kAStageBytes = kAFrags * kFragBytes;
+constexpr int kAStageBytes = kTileM * kLineBytes;      // 32 KiB
+constexpr int kRowsPerLoad = 8;    // A rows one wave instruction moves
+constexpr int kFragBytes = 1024;   // one 16 x 32 bf16 MFMA fragment
 
-// weight fragments per wave: gate/up 3 blocks x (gate, up); down 4 blocks of 32
-// rows x 2 halves
 template <bool GATEUP> struct TileShape {
-  static constexpr int kWFrags = GATEUP ? 6 : 8;
-  static constexpr int kWRows = 2 * kWFrags * 16;                  // weight rows per tile
-  static constexpr int kBFrags = 2 * kWFrags;                      // per stage
-  static constexpr int kBStageBytes = kBFrags * kFragBytes;
-  static constexpr int kBlocksPerTile = GATEUP ? 6 : 8;            // packed blocks per tile
+  static constexpr int kWRows = GATEUP ? 192 : 256;    // weight rows per tile
+  static constexpr int kBStageBytes = kWRows * kLineBytes;   // kWRows / 8 fragments
   static constexpr int kStageBytes = kAStageBytes + kBStageBytes;
-  // loads per wave per stage: A fragments, B fragments
-  static constexpr int kALoads = kAFrags / 4;
-  static constexpr int kBLoads = kBFrags / 4;
+  static constexpr int kBlocksPerTile = kWRows / 32;   // 32-row weight blocks per tile
+  static constexpr int kWP = kBlocksPerTile / 2;       // ... per wave
+  // wave instructions per stage: A (8 rows each), B (one fragment each)
+  static constexpr int kALoads = kTileM / kRowsPerLoad / 4;
+  static constexpr int kBLoads = kBStageBytes / kFragBytes / 4;
   static constexpr int kLoads = kALoads + kBLoads;
 };
 
-typedef __attribute__((address_space(3))) void* LdsPtr;
-
 // One wave instruction: 64 lanes x 16 bytes from a buffer straight into LDS at
-// `dst` + 16 * lane (dst wave-uniform).  Written as inline asm so that the
-// compiler does not treat every later LDS read as dependent on it (it would wait
-// for all outstanding loads, draining the prefetch); the kernel counts these
-// loads itself (wait_vmcnt) and orders LDS access with barriers.  The instruction
-// takes its LDS address from M0, which nothing else in these kernels uses.
-__device__ __forceinline__ void lds_dma16(Rsrc r, uint32_t voff, uint32_t soff, const void* dst) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(LdsPtr)dst);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+// byte address `m0v` + 16 * lane (m0v wave-uniform).  Written as inline asm so that
+// the compiler does not treat every later LDS read as dependent on it (it would wait
+// for all outstanding loads, draining the prefetch); the kernel counts these loads
+// itself (wait_vmcnt) and orders LDS access with barriers.  The instruction takes
+// its LDS address from M0, which nothing else in these kernels uses; one wait state
+// separates the M0 write from its use.
+__device__ __forceinline__ void lds_dma16(Rsrc r, uint32_t voff, uint32_t soff, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(m0v), "v"(voff), "s"(r), "s"(soff)
                : "memory");
@@ -77,6 +80,11 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
+// position of 16-byte chunk c of stage row r
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // Row tiles of expert e of a segment (0 if it takes the streaming path).
 __device__ __forceinline__ int seg_expert_tiles(const TileSeg& g, int e, int* lo, int* cnt) {
@@ -195,24 +203,33 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   const int row0 = s_tile[2], rows = s_tile[3];
   const int nt = s_tile[4];
   const int K = GATEUP ? d : g.inter;              // contraction length of this segment
-  const int nk = K / kTileK;                       // stages = 32-steps
+  const int nk = K / kTileK;                       // stages
 
-  // the wave index as a scalar: every load below has a wave-uniform destination
+  // LDS byte address of the stage buffers; the wave index as a scalar (every load
+  // below has a wave-uniform destination)
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(LdsPtr)&lds[0][0]);
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  // the lane's row within an 8-row load and the chunk it fetches for that row
+  const int lr = l >> 3;
+  auto load_chunk = [&](int row) { return swz_chunk(row, l & 7); };
 
-  // ---- A: row fragments rb = 4*wave + i; lane l reads row 16*rb + l%16, elements
-  // 8*(l/16) .. +7 of the stage (global: 16 rows x 64 contiguous bytes)
+  // ---- A: stage rows 8 * (kALoads * wave + i) + l / 8
   const Rsrc xr = make_rsrc(g.x, (uint64_t)g.x_rows * K * sizeof(E));
   uint32_t a_voff[S::kALoads];
 #pragma unroll
   for (int i = 0; i < S::kALoads; ++i) {
-    const int r = (wu * S::kALoads + i) * 16 + (l & 15);
+    const int r = (wu * S::kALoads + i) * kRowsPerLoad + lr;
     const int rr = row0 + min(r, rows - 1);
     const int src = (GATEUP && g.row_src) ? g.row_src[rr] / g.row_div : rr;
-    a_voff[i] = (uint32_t)(((size_t)src * K + (l >> 4) * 8) * sizeof(E));
+    a_voff[i] = (uint32_t)(((size_t)src * K + load_chunk(r) * 8) * sizeof(E));
   }
-  // ---- B: stage fragment f = kBLoads*wave + i = (block f/2, half f%2)
-  const uint32_t tb = kTileElems * sizeof(E);
+  // ---- B: the stage's weight rows in MFMA fragment order: fragment f = 2 rb + kh
+  // holds rows 16 rb .. +15 and elements 32 kh .. +31 of the stage, lane j of the
+  // fragment (16 bytes at 16 j) row j % 16, elements 8 (j / 16) .. +7.  This is the
+  // packed weight layout's own tile format, so a packed fragment is one contiguous
+  // 1 KiB read.  Row block rb is half rb % 2 of 32-row block rb / 2: for gate/up the
+  // gate (half 0) or up rows of features 96 nt + 16 (rb / 2) .. +15; for down,
+  // output columns 256 nt + 16 rb .. +15.
   const bool packed = g.packed != nullptr;
   Rsrc br0, br1;
   if (GATEUP) {
@@ -226,48 +243,52 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
                  : make_rsrc(static_cast<const E*>(g.w0) + e * ee, ee * sizeof(E));
     br1 = br0;
   }
-  uint32_t b_voff[S::kBLoads];   // per lane
-  uint32_t b_soff[S::kBLoads];   // per wave: stage-0 offset of the fragment
-  Rsrc b_rsrc[S::kBLoads];
+  const uint32_t tb = kTileElems * sizeof(E);      // one packed 16 x 32 tile
+  uint32_t b_voff[S::kBLoads];
 #pragma unroll
   for (int i = 0; i < S::kBLoads; ++i) {
     const int f = wu * S::kBLoads + i;
-    const int blk = f >> 1, half = f & 1;
-    const int pb = nt * S::kBlocksPerTile + blk;
+    const int rb = f >> 1, kh = f & 1;
+    const int blk = rb >> 1, half = rb & 1;
     if (packed) {
-      b_voff[i] = l * 8 * sizeof(E);
-      b_soff[i] = (uint32_t)(pb * nk * 2 + half) * tb;
-      b_rsrc[i] = br0;
+      // packed block pb: step j of 32 elements holds tiles 2j (half 0), 2j + 1 (half 1)
+      const int pb = nt * S::kBlocksPerTile + blk;
+      b_voff[i] = (uint32_t)((pb * nk * 4 + kh * 2 + half) * tb + l * 16);
     } else {
-      const int row = GATEUP ? pb * 16 + (l & 15) : pb * 32 + half * 16 + (l & 15);
-      b_voff[i] = (uint32_t)(((size_t)row * K + (l >> 4) * 8) * sizeof(E));
-      b_soff[i] = 0;
-      b_rsrc[i] = (GATEUP && half) ? br1 : br0;
+      const int row = GATEUP ? nt * 96 + blk * 16 + (l & 15) : nt * 256 + rb * 16 + (l & 15);
+      b_voff[i] = (uint32_t)(((size_t)row * K + kh * 32 + (l >> 4) * 8) * sizeof(E));
     }
   }
-  // per stage: packed weights advance 2 tiles, row-major 32 elements
-  const uint32_t b_step = packed ? 2 * tb : kTileK * sizeof(E);
-  const uint32_t a_step = kTileK * sizeof(E);
+  // row-major gate/up: odd row blocks are up rows
+  auto b_rsrc = [&](int i) {
+    const int f = wu * S::kBLoads + i;
+    return (GATEUP && ((f >> 1) & 1)) ? br1 : br0;
+  };
+  // per stage: packed weights advance 2 steps of (2 tiles), row-major 64 elements
+  const uint32_t b_step = packed ? 4 * tb : kLineBytes;
+  const uint32_t a_step = kLineBytes;
 
-  auto issue = [&](int kb) {
-    char* st = lds[kb % kStages];
-#pragma unroll
-    for (int i = 0; i < S::kALoads; ++i)
-      lds_dma16(xr, a_voff[i], kb * a_step, st + (wu * S::kALoads + i) * kFragBytes);
-#pragma unroll
-    for (int i = 0; i < S::kBLoads; ++i)
-      lds_dma16(b_rsrc[i], b_voff[i], b_soff[i] + kb * b_step,
-                      st + kAStageBytes + (wu * S::kBLoads + i) * kFragBytes);
+  // wave load i of stage kb (A rows first, then B rows)
+  auto issue_one = [&](int i, int kb) {
+    const uint32_t st = lds0 + (uint32_t)((kb % kStages) * S::kStageBytes);
+    if (i < S::kALoads)
+      lds_dma16(xr, a_voff[i], kb * a_step, st + (wu * S::kALoads + i) * kRowsPerLoad * kLineBytes);
+    else
+      lds_dma16(b_rsrc(i - S::kALoads), b_voff[i - S::kALoads], kb * b_step,
+                st + kAStageBytes + (wu * S::kBLoads + i - S::kALoads) * kFragBytes);
   };
 
-  // ---- wave tile: 128 rows x (kWFrags * 16) weight rows, as 32x32 MFMA blocks:
-  // kTP = 4 row pairs (two 16-row fragments each) x kWP weight pairs.
-  // v_mfma_f32_32x32x16_bf16: lane l supplies weight row l%32 and row l%32 of the
-  // token block, 8 contraction elements each; with 16-row fragments in LDS, row
-  // l%32 lives in fragment (l%32)/16 at lane (2h + l/32)*16 + l%16 for sub-step h
-  // (h = 0, 1 covers the stage's 32 elements).  Both operands use the same element
-  // assignment, so the products pair up whatever the hardware's k order.
-  constexpr int kTP = 4, kWP = S::kWFrags / 2;
+  // ---- wave tile: 128 rows x (kWP * 32) weight rows as kTP x kWP 32x32 blocks.
+  // v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32 of the weight block and
+  // of the row block, contraction elements 8 (l / 32) .. +7 of the 16-element
+  // sub-step; both operands use the same element assignment.
+  constexpr int kTP = 4, kWP = S::kWP;
+  constexpr int kSub = kTileK / 16;                  // MFMA sub-steps per stage
+  // one load of the next stage after every kEvery MFMAs: the CU's memory path then
+  // works alongside the matrix cores, and the last loads still have the remaining
+  // MFMAs of the stage to land
+  constexpr int kEvery = 3;
+  static_assert(S::kLoads * kEvery <= kSub * kTP * kWP, "loads must fit in a stage");
   const int wm = w & 1, wn = w >> 1;
   f32x16 acc[kWP][kTP];
 #pragma unroll
@@ -276,51 +297,63 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
     for (int p = 0; p < kTP; ++p)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[q][p][r] = 0.f;
-  const int half32 = (l & 31) >> 4;   // which 16-row fragment of a 32-row block
+  // a block's rows start at multiples of 32, so the swizzle depends on the lane only
+  const int lane_row = (l & 31) * kLineBytes;
+  const int lswz = ((l & 31) >> 1) & 7;
 
-  auto compute = [&](int kb) {
+  // B fragment of sub-step h for lane l: row block 2 (32-row block) + (l % 32) / 16,
+  // fragment h / 2, lane (2 (h % 2) + l / 32) * 16 + l % 16 of the fragment
+  const int bhalf = ((l & 31) >> 4) * 2 * kFragBytes;
+  auto read_frags = [&](const char* A, const char* B, int h, bf16x8 (&wf)[kWP], bf16x8 (&tf)[kTP]) {
+    const int off = lane_row + (((2 * h + (l >> 5)) ^ lswz) << 4);
+    const int boff = bhalf + (h >> 1) * kFragBytes + ((2 * (h & 1) + (l >> 5)) * 16 + (l & 15)) * 16;
+#pragma unroll
+    for (int q = 0; q < kWP; ++q)
+      wf[q] = *reinterpret_cast<const bf16x8*>(B + (wn * kWP + q) * 4 * kFragBytes + boff);
+#pragma unroll
+    for (int p = 0; p < kTP; ++p)
+      tf[p] = *reinterpret_cast<const bf16x8*>(A + (wm * kTP + p) * 32 * kLineBytes + off);
+  };
+
+  // MFMAs of stage kb; with `next`, the loads of stage kb + 1 go out in between.
+  // Operand fragments are read one sub-step ahead.
+  auto compute = [&](int kb, auto next) {
     const char* A = lds[kb % kStages];
     const char* B = A + kAStageBytes;
+    bf16x8 wf[2][kWP], tf[2][kTP];
+    read_frags(A, B, 0, wf[0], tf[0]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int lane_off = (((2 * h + (l >> 5)) * 16) + (l & 15)) * 16;
-      bf16x8 wf[kWP], tf[kTP];
-      // weight pair q: fragments (block wn*kWP + q, half 0 | 1)
-#pragma unroll
-      for (int q = 0; q < kWP; ++q)
-        wf[q] = *reinterpret_cast<const bf16x8*>(B + ((wn * kWP + q) * 2 + half32) * kFragBytes + lane_off);
-      // row pair p: fragments 8*wm + 2p + (0 | 1)
-#pragma unroll
-      for (int p = 0; p < kTP; ++p)
-        tf[p] = *reinterpret_cast<const bf16x8*>(A + (wm * 8 + 2 * p + half32) * kFragBytes + lane_off);
+    for (int h = 0; h < kSub; ++h) {
+      if (h + 1 < kSub) read_frags(A, B, h + 1, wf[(h + 1) & 1], tf[(h + 1) & 1]);
 #pragma unroll
       for (int p = 0; p < kTP; ++p)
 #pragma unroll
-        for (int q = 0; q < kWP; ++q)
-          acc[q][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[q], tf[p], acc[q][p], 0, 0, 0);
+        for (int q = 0; q < kWP; ++q) {
+          acc[q][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[h & 1][q], tf[h & 1][p], acc[q][p], 0, 0, 0);
+          const int m = (h * kTP + p) * kWP + q;
+          if (decltype(next)::value && m % kEvery == kEvery - 1 && m / kEvery < S::kLoads) {
+            // keep the load where it is: the scheduler would otherwise bunch them
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(m / kEvery, kb + 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
     }
   };
 
-  // prologue: stages 0 .. kStages-2 in flight
 #pragma unroll
-  for (int p = 0; p < kStages - 1; ++p)
-    if (p < nk) issue(p);
-  for (int kb = 0; kb < nk; ++kb) {
-    // this wave's loads of stage kb are done when at most the loads of the later
-    // stages already issued (up to kStages-2 of them) are outstanding
-    const int later = min(kStages - 2, nk - 1 - kb);
-    if (later >= 2)
-      wait_vmcnt<2 * S::kLoads>();
-    else if (later == 1)
-      wait_vmcnt<S::kLoads>();
-    else
-      wait_vmcnt<0>();
-    // every wave's loads of stage kb have landed, and every wave has finished
-    // reading the buffer that stage kb + kStages - 1 now overwrites
+  for (int i = 0; i < S::kLoads; ++i) issue_one(i, 0);
+  for (int kb = 0; kb + 1 < nk; ++kb) {
+    // this wave's loads of stage kb have landed ...
+    wait_vmcnt<0>();
+    // ... and so have every wave's; every wave has also finished reading the buffer
+    // that stage kb + 1 now overwrites
     barrier_only();
-    if (kb + kStages - 1 < nk) issue(kb + kStages - 1);
-    compute(kb);
+    compute(kb, std::true_type{});
   }
+  wait_vmcnt<0>();
+  barrier_only();
+  compute(nk - 1, std::false_type{});
 
   // ---- epilogue ----------------------------------------------------------------
   // acc[q][p]: lane l, register r holds weight row 8*(r/4) + 4*(l/32) + r%4 of pair
