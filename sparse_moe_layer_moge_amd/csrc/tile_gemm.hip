@@ -23,11 +23,12 @@
 // The loads of stage k + 1 are spread between the MFMAs of stage k; a stage
 // boundary is a wait for the wave's own loads plus a workgroup barrier.
 //
-// The tiles of all experts form one list: for every expert above the threshold
-// ceil(rows / 256) row tiles, each paired with every weight tile; the shared
-// segment's tiles follow.  The list is built on the device from the expert
-// offsets (no host synchronisation).  Consecutive list entries share the row tile
-// and go to the same XCD, so an activation tile is read from one L2.
+// The tiles of a segment form one list: for every expert above the threshold
+// ceil(rows / 256) row tiles, each paired with every weight tile.  The list is
+// built on the device from the expert offsets (no host synchronisation).  Each XCD
+// takes a contiguous eighth of every segment's list, so consecutive entries (same
+// row tile, neighbouring weight tiles) share one L2; the segment with the longer
+// contraction is scheduled first.
 #include <limits.h>
 
 #include <type_traits>
@@ -168,24 +169,28 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
     const int ntb = b.n_exp ? (GATEUP ? b.inter / (S::kWRows / 2) : d / S::kWRows) : 0;
     const int ma = seg_total_tiles(a);
     const int mb = b.n_exp ? seg_total_tiles(b) : 0;
-    const int total = ma * nta + mb * ntb;
-    const int chunk = (total + kXcds - 1) / kXcds;
+    // every XCD takes an equal share of each segment; the segment with the longer
+    // contraction (more work per tile) goes first, so its tiles do not pile up at
+    // the end of the launch
+    const bool b_first = (GATEUP ? d : b.inter) > (GATEUP ? d : a.inter);
+    const int tot0 = b_first ? mb * ntb : ma * nta, tot1 = b_first ? ma * nta : mb * ntb;
+    const int ch0 = (tot0 + kXcds - 1) / kXcds, ch1 = (tot1 + kXcds - 1) / kXcds;
     const int x = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
-    const int t = x * chunk + i;
     int seg = -1, e = 0, row0 = 0, rows = 0, nt = 0;
-    if (i < chunk && t < total) {
-      bool found;
-      if (t < ma * nta) {
-        seg = 0;
-        nt = t % nta;
-        found = seg_find_tile(a, t / nta, &e, &row0, &rows);
-      } else {
-        seg = 1;
-        const int u = t - ma * nta;
-        nt = u % ntb;
-        found = seg_find_tile(b, u / ntb, &e, &row0, &rows);
-      }
-      if (!found || rows <= 0) seg = -1;
+    int which = -1, t = 0;
+    if (i < ch0) {
+      t = x * ch0 + i;
+      if (t < tot0) which = 0;
+    } else if (i - ch0 < ch1) {
+      t = x * ch1 + (i - ch0);
+      if (t < tot1) which = 1;
+    }
+    if (which >= 0) {
+      seg = (which == 0) == b_first ? 1 : 0;
+      const TileSeg& g = seg ? b : a;
+      const int ntg = seg ? ntb : nta;
+      nt = t % ntg;
+      if (!seg_find_tile(g, t / ntg, &e, &row0, &rows) || rows <= 0) seg = -1;
     }
     if (l == 0) {
       s_tile[0] = seg;
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   // one load of the next stage after every kEvery MFMAs: the CU's memory path then
   // works alongside the matrix cores, and the last loads still have the remaining
   // MFMAs of the stage to land
-  constexpr int kEvery = 3;
+  constexpr int kEvery = GATEUP ? 2 : 3;
   static_assert(S::kLoads * kEvery <= kSub * kTP * kWP, "loads must fit in a stage");
   const int wm = w & 1, wn = w >> 1;
   f32x16 acc[kWP][kTP];
@@ -409,9 +414,11 @@ hipError_t launch_ffn_tile(bool gateup, int d, const TileSeg& a, const TileSeg* 
   const long long wa = gateup ? TileShape<true>::kWRows / 2 : TileShape<false>::kWRows;
   const long long nta = gateup ? a.inter / wa : d / wa;
   const long long ntb = b ? (gateup ? bb.inter / wa : d / wa) : 0;
-  const long long bound = tile_bound(a) * nta + tile_bound(bb) * ntb;
-  if (bound == 0) return hipSuccess;
-  const long long grid = ((bound + kXcds - 1) / kXcds) * kXcds;
+  // each segment's tiles are spread over the XCDs separately
+  const long long ba = tile_bound(a) * nta, bbn = tile_bound(bb) * ntb;
+  const long long per_xcd = (ba + kXcds - 1) / kXcds + (bbn + kXcds - 1) / kXcds;
+  if (per_xcd == 0) return hipSuccess;
+  const long long grid = per_xcd * kXcds;
   if (grid > INT_MAX) return hipErrorInvalidValue;
   if (gateup)
     hipLaunchKernelGGL(k_ffn_tile<true>, dim3((unsigned)grid), dim3(kTileThreads), 0, st, a, bb, d);
