@@ -42,7 +42,8 @@ namespace moge {
 constexpr int kTileM = 256;        // rows per tile
 constexpr int kTileK = 64;         // contraction elements per stage
 constexpr int kLineBytes = kTileK * 2;  // one operand row of a stage (bf16)
-constexpr int kStages = 2;         // LDS buffers
+constexpr int kABufs = 2;          // activation stages in LDS (loaded one stage ahead)
+constexpr int kBBufs = 3;          // weight stages in LDS (loaded two stages ahead)
 constexpr int kTileThreads = 256;  // 4 waves: 2 (rows) x 2 (weight rows)
 constexpr int kXcds = 8;
 constexpr int kAStageBytes = kTileM * kLineBytes;      // 32 KiB
@@ -52,7 +53,7 @@ constexpr int kFragBytes = 1024;   // one 16 x 32 bf16 MFMA fragment
 template <bool GATEUP> struct TileShape {
   static constexpr int kWRows = GATEUP ? 192 : 256;    // weight rows per tile
   static constexpr int kBStageBytes = kWRows * kLineBytes;   // kWRows / 8 fragments
-  static constexpr int kStageBytes = kAStageBytes + kBStageBytes;
+  static constexpr int kLdsBytes = kABufs * kAStageBytes + kBBufs * kBStageBytes;
   static constexpr int kBlocksPerTile = kWRows / 32;   // 32-row weight blocks per tile
   static constexpr int kWP = kBlocksPerTile / 2;       // ... per wave
   // wave instructions per stage: A (8 rows each), B (one fragment each)
@@ -158,8 +159,12 @@ template <bool GATEUP>
 __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
   typedef bf16 E;
   typedef TileShape<GATEUP> S;
-  __shared__ __attribute__((aligned(1024))) char lds[kStages][S::kStageBytes];
-  __shared__ int s_tile[5];
+  static_assert(S::kLdsBytes <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char lds[S::kLdsBytes];
+  // the tile descriptor lives in the last weight buffer, which the first loads
+  // (stages 0 and 1) leave alone and stage 2's loads overwrite only after the first
+  // barrier of the main loop
+  int* s_tile = reinterpret_cast<int*>(lds + kABufs * kAStageBytes + (kBBufs - 1) * S::kBStageBytes);
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
 
   // LDS byte address of the stage buffers; the wave index as a scalar (every load
   // below has a wave-uniform destination)
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(LdsPtr)&lds[0][0]);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(LdsPtr)&lds[0]);
   const int wu = __builtin_amdgcn_readfirstlane(w);
   // the lane's row within an 8-row load and the chunk it fetches for that row
   const int lr = l >> 3;
@@ -273,14 +278,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   const uint32_t b_step = packed ? 4 * tb : kLineBytes;
   const uint32_t a_step = kLineBytes;
 
-  // wave load i of stage kb (A rows first, then B rows)
-  auto issue_one = [&](int i, int kb) {
-    const uint32_t st = lds0 + (uint32_t)((kb % kStages) * S::kStageBytes);
-    if (i < S::kALoads)
-      lds_dma16(xr, a_voff[i], kb * a_step, st + (wu * S::kALoads + i) * kRowsPerLoad * kLineBytes);
-    else
-      lds_dma16(b_rsrc(i - S::kALoads), b_voff[i - S::kALoads], kb * b_step,
-                st + kAStageBytes + (wu * S::kBLoads + i - S::kALoads) * kFragBytes);
+  // wave load i of the A rows of stage kb, and of the B rows
+  auto issue_a = [&](int i, int kb) {
+    const uint32_t st = lds0 + (uint32_t)((kb % kABufs) * kAStageBytes);
+    lds_dma16(xr, a_voff[i], kb * a_step, st + (wu * S::kALoads + i) * kRowsPerLoad * kLineBytes);
+  };
+  auto issue_b = [&](int i, int kb) {
+    const uint32_t st = lds0 + (uint32_t)(kABufs * kAStageBytes + (kb % kBBufs) * S::kBStageBytes);
+    lds_dma16(b_rsrc(i), b_voff[i], kb * b_step, st + (wu * S::kBLoads + i) * kFragBytes);
   };
 
   // ---- wave tile: 128 rows x (kWP * 32) weight rows as kTP x kWP 32x32 blocks.
@@ -293,7 +298,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   // works alongside the matrix cores, and the last loads still have the remaining
   // MFMAs of the stage to land
   constexpr int kEvery = GATEUP ? 2 : 3;
-  static_assert(S::kLoads * kEvery <= kSub * kTP * kWP, "loads must fit in a stage");
+  static_assert((S::kALoads + S::kBLoads) * kEvery <= kSub * kTP * kWP, "loads must fit in a stage");
   const int wm = w & 1, wn = w >> 1;
   f32x16 acc[kWP][kTP];
 #pragma unroll
@@ -320,11 +325,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       tf[p] = *reinterpret_cast<const bf16x8*>(A + (wm * kTP + p) * 32 * kLineBytes + off);
   };
 
-  // MFMAs of stage kb; with `next`, the loads of stage kb + 1 go out in between.
-  // Operand fragments are read one sub-step ahead.
-  auto compute = [&](int kb, auto next) {
-    const char* A = lds[kb % kStages];
-    const char* B = A + kAStageBytes;
+  // MFMAs of stage kb.  In between go out (every kEvery MFMAs, A first) the A
+  // loads of stage kb + 1 when `next_a`, and the B loads of stage kb + 2 when
+  // `next_b`.  Operand fragments are read one sub-step ahead.
+  auto compute = [&](int kb, auto next_a, auto next_b) {
+    constexpr int na = decltype(next_a)::value ? S::kALoads : 0;
+    constexpr int nl = na + (decltype(next_b)::value ? S::kBLoads : 0);
+    const char* A = lds + (kb % kABufs) * kAStageBytes;
+    const char* B = lds + kABufs * kAStageBytes + (kb % kBBufs) * S::kBStageBytes;
     bf16x8 wf[2][kWP], tf[2][kTP];
     read_frags(A, B, 0, wf[0], tf[0]);
 #pragma unroll
@@ -336,29 +344,46 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
         for (int q = 0; q < kWP; ++q) {
           acc[q][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[h & 1][q], tf[h & 1][p], acc[q][p], 0, 0, 0);
           const int m = (h * kTP + p) * kWP + q;
-          if (decltype(next)::value && m % kEvery == kEvery - 1 && m / kEvery < S::kLoads) {
+          const int j = m / kEvery;
+          if (m % kEvery == kEvery - 1 && j < nl) {
             // keep the load where it is: the scheduler would otherwise bunch them
             __builtin_amdgcn_sched_barrier(0);
-            issue_one(m / kEvery, kb + 1);
+            if (j < na)
+              issue_a(j, kb + 1);
+            else
+              issue_b(j - na, kb + 2);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
     }
   };
 
+  // Loads complete in issue order as far as vmcnt is concerned.  At the top of
+  // stage kb the youngest loads are stage kb + 1's B rows (kBLoads of them), issued
+  // after stage kb's A rows; everything older has to be in.
 #pragma unroll
-  for (int i = 0; i < S::kLoads; ++i) issue_one(i, 0);
-  for (int kb = 0; kb + 1 < nk; ++kb) {
-    // this wave's loads of stage kb have landed ...
-    wait_vmcnt<0>();
-    // ... and so have every wave's; every wave has also finished reading the buffer
-    // that stage kb + 1 now overwrites
+  for (int i = 0; i < S::kALoads; ++i) issue_a(i, 0);
+#pragma unroll
+  for (int i = 0; i < S::kBLoads; ++i) issue_b(i, 0);
+  if (nk > 1) {
+#pragma unroll
+    for (int i = 0; i < S::kBLoads; ++i) issue_b(i, 1);
+  }
+  for (int kb = 0; kb + 2 < nk; ++kb) {
+    wait_vmcnt<S::kBLoads>();
+    // every wave's loads of stage kb are in, and every wave has finished reading
+    // the buffers the loads issued during this stage overwrite (stage kb - 1's)
     barrier_only();
-    compute(kb, std::true_type{});
+    compute(kb, std::true_type{}, std::true_type{});
+  }
+  if (nk > 1) {
+    wait_vmcnt<S::kBLoads>();
+    barrier_only();
+    compute(nk - 2, std::true_type{}, std::false_type{});
   }
   wait_vmcnt<0>();
   barrier_only();
-  compute(nk - 1, std::false_type{});
+  compute(nk - 1, std::false_type{}, std::false_type{});
 
   // ---- epilogue ----------------------------------------------------------------
   // acc[q][p]: lane l, register r holds weight row 8*(r/4) + 4*(l/32) + r%4 of pair
