@@ -11,15 +11,33 @@
 //   3. per chunk, the ballot masks again; the rank of a token among the chunk's
 //      tokens that chose expert e is popcount(mask_e & lanes-below-me), so rows
 //      come out in token order.
-// Up to kSmallChunks chunks run in one workgroup (one launch, all counts in LDS);
-// larger batches use a three-kernel version with the same arithmetic.
+// Small batches run in one workgroup (one launch, all counts in LDS); larger ones
+// use a three-kernel version with the same arithmetic, parallel over chunks.
 #include "moge_common.hpp"
 #include "moge_internal.hpp"
 
 namespace moge {
 
 constexpr int kSmallWaves = 16;    // waves of the single-workgroup kernel
-constexpr int kSmallChunks = 64;   // chunks it handles (T <= 4096)
+constexpr int kSmallChunks = 64;   // chunks it can hold (T <= 4096)
+constexpr int kSmallUseChunks = 8; // chunks up to which it is used: beyond that the
+                                   // chunk-parallel kernels finish sooner
+
+// f(k, e) for every slot k of token t, in slot order.  The slot indices are
+// loaded 8 at a time before any is used, so a token's loads overlap instead of
+// paying one memory latency each.
+template <typename F>
+__device__ __forceinline__ void for_each_slot(const int32_t* __restrict__ idx, int t, int K, F&& f) {
+  const int32_t* p = idx + (size_t)t * K;
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    int e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (k0 + j < K) ? p[k0 + j] : -1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < K) f(k0 + j, e[j]);
+  }
+}
 
 // The set of experts token t chose (entries outside [0, N) and repeats ignored;
 // moge_route never produces either).
@@ -27,10 +45,9 @@ __device__ __forceinline__ void chosen_set(const int32_t* __restrict__ idx, int 
                                            bool valid, uint64_t (&chosen)[4]) {
   chosen[0] = chosen[1] = chosen[2] = chosen[3] = 0ull;
   if (!valid) return;
-  for (int k = 0; k < K; ++k) {
-    const int e = idx[(size_t)t * K + k];
+  for_each_slot(idx, t, K, [&](int, int e) {
     if ((unsigned)e < (unsigned)N) chosen[e >> 6] |= 1ull << (e & 63);
-  }
+  });
 }
 
 __device__ __forceinline__ bool in_set(const uint64_t (&s)[4], int e) {
@@ -57,8 +74,7 @@ __device__ __forceinline__ void chunk_scatter(const int32_t* __restrict__ idx, i
   if (!valid) return;
   const uint64_t lt = lanemask_lt();
   uint64_t seen[4] = {0ull, 0ull, 0ull, 0ull};
-  for (int k = 0; k < K; ++k) {
-    const int e = idx[(size_t)t * K + k];
+  for_each_slot(idx, t, K, [&](int k, int e) {
     int row = -1;
     if ((unsigned)e < (unsigned)N && !in_set(seen, e)) {
       seen[e >> 6] |= 1ull << (e & 63);
@@ -66,7 +82,55 @@ __device__ __forceinline__ void chunk_scatter(const int32_t* __restrict__ idx, i
       sorted_pair[row] = t * K + k;
     }
     pair_row[(size_t)t * K + k] = row;
+  });
+}
+
+// inclusive prefix sum across the 64 lanes of a wave
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (l >= o) v += u;
   }
+  return v;
+}
+
+// How many of one chunk's tokens chose each expert: dst[e] for e < N (one wave).
+__device__ __forceinline__ void chunk_counts(const uint64_t (&chosen)[4], int N,
+                                             int32_t* __restrict__ dst) {
+  const int l = threadIdx.x & 63;
+  for (int q = 0; q * 64 < N; ++q) {
+    int mine = 0;
+    const int n = min(64, N - q * 64);
+    for (int j = 0; j < n; ++j) {
+      const int c = __popcll(__ballot(in_set(chosen, q * 64 + j)));
+      if (l == j) mine = c;
+    }
+    if (l < n) dst[q * 64 + l] = mine;
+  }
+}
+
+// offsets[e] = exclusive prefix of counts over experts (N <= 256, one wave: lane l
+// owns experts 4l .. 4l+3); the total lands in off[N]
+__device__ __forceinline__ void expert_offsets(const int32_t* cnt, int N, int32_t* off) {
+  const int l = threadIdx.x & 63;
+  int v[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * l + i;
+    v[i] = e < N ? cnt[e] : 0;
+    s += v[i];
+  }
+  const int incl = wave_incl_scan(s);
+  int run = incl - s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * l + i;
+    if (e < N) off[e] = run;
+    run += v[i];
+  }
+  if (l == 63) off[N] = incl;
 }
 
 // ---------------------------------------------------------------------------
@@ -83,44 +147,29 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_permute_small(
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int nchunks = (T + 63) / 64;
 
+  // per chunk and expert: tokens of the chunk that chose the expert
   for (int c = w; c < nchunks; c += kSmallWaves) {
-    const int t = c * 64 + l;
     uint64_t chosen[4];
-    chosen_set(idx, t, K, N, t < T, chosen);
-    for (int e = 0; e < N; ++e) {
-      const uint64_t m = __ballot(in_set(chosen, e));
-      if (l == 0) s_base[c][e] = __popcll(m);
+    chosen_set(idx, c * 64 + l, K, N, c * 64 + l < T, chosen);
+    chunk_counts(chosen, N, s_base[c]);
+  }
+  __syncthreads();
+  // per expert: exclusive prefix over the chunks (lane = chunk), total = count
+  for (int e = w; e < N; e += kSmallWaves) {
+    const int v = l < nchunks ? s_base[l][e] : 0;
+    const int incl = wave_incl_scan(v);
+    if (l < nchunks) s_base[l][e] = incl - v;
+    if (l == 63) {
+      s_cnt[e] = incl;
+      counts[e] = incl;
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < N; e += blockDim.x) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = s_base[c][e];
-      s_base[c][e] = run;
-      run += v;
-    }
-    s_cnt[e] = run;
-    counts[e] = run;
-  }
+  if (w == 0) expert_offsets(s_cnt, N, s_off);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int e = 0; e < N; ++e) {
-      s_off[e] = acc;
-      offsets[e] = acc;
-      acc += s_cnt[e];
-    }
-    s_off[N] = acc;
-    offsets[N] = acc;
-  }
+  for (int e = threadIdx.x; e <= N; e += blockDim.x) offsets[e] = s_off[e];
   const int G = N / M;
-  for (int g = threadIdx.x; g < M; g += blockDim.x) {
-    int sum = 0;
-    for (int q = 0; q < G; ++q) sum += s_cnt[g * G + q];
-    group_counts[g] = sum;
-  }
-  __syncthreads();
+  for (int g = threadIdx.x; g < M; g += blockDim.x) group_counts[g] = s_off[(g + 1) * G] - s_off[g * G];
   for (int c = w; c < nchunks; c += kSmallWaves) {
     const int t = c * 64 + l;
     uint64_t chosen[4];
@@ -142,64 +191,56 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_permute_small(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_chunk_hist(const int32_t* __restrict__ idx, int T, int K,
                                                    int N, int32_t* __restrict__ blk_cnt) {
-  const int l = threadIdx.x;
-  const int t = blockIdx.x * 64 + l;
+  const int t = blockIdx.x * 64 + threadIdx.x;
   uint64_t chosen[4];
   chosen_set(idx, t, K, N, t < T, chosen);
-  int32_t* out = blk_cnt + (size_t)blockIdx.x * N;
-  for (int e = 0; e < N; ++e) {
-    const uint64_t m = __ballot(in_set(chosen, e));
-    if (l == 0) out[e] = __popcll(m);
-  }
+  chunk_counts(chosen, N, blk_cnt + (size_t)blockIdx.x * N);
 }
 
-__global__ __launch_bounds__(256) void k_scan(const int32_t* __restrict__ blk_cnt, int nblk,
-                                              int N, int M, int32_t* __restrict__ counts,
-                                              int32_t* __restrict__ offsets,
-                                              int32_t* __restrict__ group_counts,
-                                              int32_t* __restrict__ blk_base) {
-  __shared__ int s_cnt[256];
-  const int e = threadIdx.x;
-  if (e < N) {
-    int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      blk_base[(size_t)b * N + e] = run;
-      run += blk_cnt[(size_t)b * N + e];
-    }
-    counts[e] = run;
-    s_cnt[e] = run;
+// one workgroup per expert: exclusive prefix of its chunk counts, and its total
+__global__ __launch_bounds__(256) void k_scan_chunks(const int32_t* __restrict__ blk_cnt, int nblk,
+                                                     int N, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ blk_base) {
+  __shared__ int s_sum[4];
+  const int e = blockIdx.x;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  int carry = 0;
+  for (int b0 = 0; b0 < nblk; b0 += 256) {
+    const int b = b0 + threadIdx.x;
+    const int v = b < nblk ? blk_cnt[(size_t)b * N + e] : 0;
+    const int incl = wave_incl_scan(v);
+    if (l == 63) s_sum[w] = incl;
+    __syncthreads();
+    int before = carry;
+    for (int q = 0; q < w; ++q) before += s_sum[q];
+    if (b < nblk) blk_base[(size_t)b * N + e] = before + incl - v;
+    carry += s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
+    __syncthreads();
   }
-  __syncthreads();
-  if (e == 0) {
-    int acc = 0;
-    for (int q = 0; q < N; ++q) {
-      offsets[q] = acc;
-      acc += s_cnt[q];
-    }
-    offsets[N] = acc;
-  }
-  const int G = N / M;
-  for (int g = e; g < M; g += 256) {
-    int s = 0;
-    for (int q = 0; q < G; ++q) s += s_cnt[g * G + q];
-    group_counts[g] = s;
-  }
+  if (threadIdx.x == 0) counts[e] = carry;
 }
 
 __global__ __launch_bounds__(64) void k_chunk_scatter(const int32_t* __restrict__ idx, int T,
-                                                      int K, int N,
-                                                      const int32_t* __restrict__ offsets,
+                                                      int K, int N, int M,
+                                                      const int32_t* __restrict__ counts,
                                                       const int32_t* __restrict__ blk_base,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ group_counts,
                                                       int32_t* __restrict__ sorted_pair,
                                                       int32_t* __restrict__ pair_row) {
   __shared__ uint64_t s_mask[256];
-  __shared__ int32_t s_off[256];
+  __shared__ int32_t s_off[257];
   __shared__ int32_t s_base[256];
   const int l = threadIdx.x;
   const int t = blockIdx.x * 64 + l;
-  for (int e = l; e < N; e += 64) {
-    s_off[e] = offsets[e];
-    s_base[e] = blk_base[(size_t)blockIdx.x * N + e];
+  // expert offsets from the totals (every workgroup; the first one publishes them)
+  expert_offsets(counts, N, s_off);
+  for (int e = l; e < N; e += 64) s_base[e] = blk_base[(size_t)blockIdx.x * N + e];
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int e = l; e <= N; e += 64) offsets[e] = s_off[e];
+    const int G = N / M;
+    for (int g = l; g < M; g += 64) group_counts[g] = s_off[(g + 1) * G] - s_off[g * G];
   }
   uint64_t chosen[4];
   chosen_set(idx, t, K, N, t < T, chosen);
@@ -213,16 +254,15 @@ hipError_t launch_permute(const int32_t* idx, int T, int K, int N, int M, int32_
                           int32_t* group_counts, int32_t* sorted_pair, int32_t* pair_row,
                           hipStream_t st) {
   const int nblk = perm_blocks(T);
-  if (nblk <= kSmallChunks) {
+  if (nblk <= kSmallUseChunks) {
     hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(64 * kSmallWaves), 0, st, idx, T, K, N, M,
                        counts, offsets, group_counts, sorted_pair, pair_row);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_chunk_hist, dim3(nblk), dim3(64), 0, st, idx, T, K, N, blk_cnt);
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(256), 0, st, blk_cnt, nblk, N, M, counts, offsets,
-                     group_counts, blk_base);
-  hipLaunchKernelGGL(k_chunk_scatter, dim3(nblk), dim3(64), 0, st, idx, T, K, N, offsets,
-                     blk_base, sorted_pair, pair_row);
+  hipLaunchKernelGGL(k_scan_chunks, dim3(N), dim3(256), 0, st, blk_cnt, nblk, N, counts, blk_base);
+  hipLaunchKernelGGL(k_chunk_scatter, dim3(nblk), dim3(64), 0, st, idx, T, K, N, M, counts,
+                     blk_base, offsets, group_counts, sorted_pair, pair_row);
   return hipGetLastError();
 }
 
