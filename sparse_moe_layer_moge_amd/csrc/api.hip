@@ -182,38 +182,51 @@ moge::TileSeg tile_view(const moge::FfnSeg& f, bool gateup) {
   return t;
 }
 
-// Both projections of up to two segments: the streaming kernels take experts with
-// at most `thr` rows, the tile kernels the others (launched only when some expert
-// can have more: an expert never has more rows than the batch has tokens).
+// Both projections of up to two segments.  The streaming kernels take routed
+// experts with at most kStreamMaxRows rows (the shared segment up to
+// kSharedStreamMaxRows), the 64-row tile kernels those with up to
+// kSmallTileMaxRows, the 256-row tile kernels the rest.  A tile launch is made only
+// when some expert can fall in its range (an expert never has more rows than the
+// batch has tokens).
 moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh,
                       hipStream_t st, bool marks) {
   // the tile path covers bf16 and its tile shapes; everything else streams
   const bool tiles_ok = dtype == MOGE_BF16 && moge::tile_path_ok(d, routed.inter) &&
                         (!sh || moge::tile_path_ok(d, sh->inter));
   const int thr = tiles_ok ? moge::kStreamMaxRows : INT_MAX;
+  const int sh_thr = tiles_ok ? moge::kSharedStreamMaxRows : INT_MAX;
+  const int thr_big = moge::kSmallTileMaxRows;
   routed.thr = thr;
-  const bool big = T > thr;
-  const bool sh_tile = sh && sh->rows > thr;
-  if (sh) sh->thr = thr;
-  moge::FfnSeg* sh_stream = (sh && !sh_tile) ? sh : nullptr;
-  CHECK(hip_check(moge::launch_ffn_gateup(dtype, d, routed, sh_stream, st), "expert gate/up"));
-  if (big) {
-    const moge::TileSeg a = tile_view(routed, true);
-    moge::TileSeg b;
-    if (sh_tile) b = tile_view(*sh, true);
-    CHECK(hip_check(moge::launch_ffn_tile(true, d, a, sh_tile ? &b : nullptr, st),
-                    "expert gate/up tiles"));
+  if (sh) sh->thr = sh_thr;
+  const bool sh_stream = sh && sh->rows <= sh_thr;
+  // tile launches: `lo < rows <= hi`
+  struct Range { bool on; int lo, hi; bool big; };
+  const Range ranges[2] = {{tiles_ok && T > thr, thr, thr_big, false},
+                           {tiles_ok && T > thr_big, thr_big, INT_MAX, true}};
+  for (int gateup = 1; gateup >= 0; --gateup) {
+    if (gateup)
+      CHECK(hip_check(moge::launch_ffn_gateup(dtype, d, routed, sh_stream ? sh : nullptr, st),
+                      "expert gate/up"));
+    else
+      CHECK(hip_check(moge::launch_ffn_down(dtype, d, routed, sh_stream ? sh : nullptr, st),
+                      "expert down"));
+    for (const Range& rg : ranges) {
+      if (!rg.on) continue;
+      moge::TileSeg a = tile_view(routed, gateup);
+      a.thr = rg.lo;
+      a.thr_hi = rg.hi;
+      const bool sh_here = sh && !sh_stream && sh->rows > rg.lo && sh->rows <= rg.hi;
+      moge::TileSeg b;
+      if (sh_here) {
+        b = tile_view(*sh, gateup);
+        b.thr = rg.lo;
+        b.thr_hi = rg.hi;
+      }
+      CHECK(hip_check(moge::launch_ffn_tile(gateup, rg.big, d, a, sh_here ? &b : nullptr, st),
+                      gateup ? "expert gate/up tiles" : "expert down tiles"));
+    }
+    if (marks) mark(gateup ? 4 : 5, st);
   }
-  if (marks) mark(4, st);
-  CHECK(hip_check(moge::launch_ffn_down(dtype, d, routed, sh_stream, st), "expert down"));
-  if (big) {
-    const moge::TileSeg a = tile_view(routed, false);
-    moge::TileSeg b;
-    if (sh_tile) b = tile_view(*sh, false);
-    CHECK(hip_check(moge::launch_ffn_tile(false, d, a, sh_tile ? &b : nullptr, st),
-                    "expert down tiles"));
-  }
-  if (marks) mark(5, st);
   return MOGE_OK;
 }
 

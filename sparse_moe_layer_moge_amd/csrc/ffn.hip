@@ -214,18 +214,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_
 // launchers
 // ---------------------------------------------------------------------------
 // Resident wave slots of the streaming kernels (3 waves per SIMD, 4 SIMDs per CU).
-static int stream_slots() {
+int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 3 * 4 * 256;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   if (cus[dev] == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
     cus[dev] = n;
   }
-  return 3 * 4 * cus[dev];
+  return cus[dev];
 }
+
+static int stream_slots() { return 3 * 4 * device_cus(); }
 
 // Blocks per wave for one segment: the divisor k <= 8 of its blocks per expert
 // whose item size (k blocks) is closest to an even share of the launch's weight

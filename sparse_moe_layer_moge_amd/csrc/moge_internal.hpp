@@ -29,6 +29,9 @@ hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* sorted_pa
                               const int32_t* offsets_end, int R, int K, int d, void* x_perm,
                               hipStream_t st);
 
+// compute units of the current device (cached per device)
+int device_cus();
+
 // ---- expert FFN (ffn.hip) --------------------------------------------------
 // One segment = a set of SwiGLU experts sharing a weight layout.  Row r of the
 // segment reads activation row x[row_src ? row_src[r] / row_div : r].  Expert e
@@ -59,8 +62,14 @@ hipError_t launch_ffn_gateup(int dtype, int d, const FfnSeg& a, const FfnSeg* b,
 hipError_t launch_ffn_down(int dtype, int d, const FfnSeg& a, const FfnSeg* b, hipStream_t st);
 
 // ---- expert FFN, MFMA tile path (tile_gemm.hip, bf16) ----------------------
-// Experts with more than `thr` rows: 128-row x 128-weight-row tiles through LDS.
-constexpr int kStreamMaxRows = 64;  // the streaming path's row limit (4 row subtiles)
+// Routed experts with at most kStreamMaxRows rows take the streaming kernels; those
+// with more take 64-row MFMA tiles up to kSmallTileMaxRows rows and 256-row tiles
+// beyond.  The shared experts (one segment of T rows) stream up to
+// kSharedStreamMaxRows: at small T their few weight tiles would leave most CUs idle,
+// while in the streaming launch they share the CUs with the routed experts.
+constexpr int kStreamMaxRows = 32;
+constexpr int kSharedStreamMaxRows = 64;
+constexpr int kSmallTileMaxRows = 128;
 struct TileSeg {
   const void* x = nullptr;         // activation rows (x, or H for the down projection)
   int x_rows = 0;
@@ -70,13 +79,16 @@ struct TileSeg {
   int rows = 0;
   int n_exp = 0;
   int inter = 0;
-  int thr = 0;                     // experts with more rows than this take the tile path
+  int thr = 0;                     // the launch covers experts with more rows than
+  int thr_hi = 0x7fffffff;         // thr and at most thr_hi
   const void* w0 = nullptr;        // row-major: gate (gate/up) or down
   const void* w1 = nullptr;        // row-major: up (gate/up)
   const void* packed = nullptr;    // packed part (expert-strided), or nullptr
   void* out = nullptr;             // H (gate/up) or y (down)
 };
-hipError_t launch_ffn_tile(bool gateup, int d, const TileSeg& a, const TileSeg* b, hipStream_t st);
+// big: 256-row tiles; otherwise 64-row tiles
+hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const TileSeg* b,
+                           hipStream_t st);
 // shapes the tile kernels cover (96-feature gate/up tiles, 256-column down tiles)
 bool tile_path_ok(int d, int inter);
 

@@ -1,34 +1,41 @@
 // MFMA tile path of the grouped expert FFN, for experts whose row count is above
-// the streaming threshold (prefill batches; the shared experts of a large batch).
+// the streaming threshold (mid-size decode batches, prefill batches, the shared
+// experts of a large batch).
 //
 // The TechWalker page (section 三, SwiftGMM) has the grouped matmul switch between
-// a GEMV-like and a GEMM-like mode by workload; this is the GEMM-like mode.  Each
-// workgroup (4 waves, one per SIMD) computes one tile of 256 rows:
-//   gate/up: 96 intermediate features (their 96 gate and 96 up weight rows), SwiGLU
-//            in the epilogue, H rounded once;
-//   down:    256 output columns.
-// Every wave owns 128 rows x (96 | 128) weight rows as 4 x (3 | 4) blocks of 32x32
-// float32 accumulators (v_mfma_f32_32x32x16_bf16).
+// a GEMV-like and a GEMM-like mode by workload; these are the GEMM-like modes.  A
+// workgroup has 4 waves (one per SIMD) and computes one tile; there are two tile
+// shapes, chosen per expert by its row count:
+//   big   (above 128 rows): 256 rows x (96 gate/up features | 256 output columns);
+//         waves 2 (rows) x 2 (weight rows), each 128 rows x (96 | 128) weight rows
+//         as 4 x (3 | 4) blocks of 32x32 float32 accumulators.  This one is bound
+//         by the matrix cores.
+//   small (up to 128 rows): 64 rows x (64 gate/up features | 128 output columns);
+//         all four waves on the same 64 rows, each with its own 32 weight rows.
+//         This one streams each expert's weights once and is bound by HBM.
+// gate/up applies SwiGLU in the epilogue and rounds H once.  The matrix
+// instruction is v_mfma_f32_32x32x16_bf16.
 //
-// The contraction runs in stages of 64 elements through two LDS buffers, filled
-// straight from global memory (buffer loads with the LDS destination).  What makes
-// these loads fast is that every 16-lane quarter of a wave instruction reads whole
-// 128-byte lines:
+// The contraction runs in stages of 64 elements through rings of LDS buffers,
+// filled straight from global memory (buffer loads with the LDS destination).
+// Every 16-lane quarter of such a wave instruction reads whole 128-byte lines:
 //   A (activation rows): 8 rows x 128 bytes per instruction, each row's line stored
 //     with its eight 16-byte chunks XOR-swizzled by the row index (chunk c of row r
 //     at position c ^ ((r >> 1) & 7)), so the MFMA operand reads are free of bank
 //     conflicts;
 //   B (weight rows): in MFMA fragment order, one 16-row x 32-element fragment (1 KiB,
 //     contiguous in the packed weight layout) per instruction.
-// The loads of stage k + 1 are spread between the MFMAs of stage k; a stage
-// boundary is a wait for the wave's own loads plus a workgroup barrier.
+// The loads of later stages are spread between the MFMAs of the current one; a
+// stage boundary is a wait for the wave's own loads plus a workgroup barrier.  The
+// big tile keeps 2 activation and 3 weight stages in LDS; the small tile keeps 6 of
+// both, enough bytes in flight to cover HBM latency with one workgroup per CU.
 //
-// The tiles of a segment form one list: for every expert above the threshold
-// ceil(rows / 256) row tiles, each paired with every weight tile.  The list is
-// built on the device from the expert offsets (no host synchronisation).  Each XCD
-// takes a contiguous eighth of every segment's list, so consecutive entries (same
-// row tile, neighbouring weight tiles) share one L2; the segment with the longer
-// contraction is scheduled first.
+// The tiles of a segment form one list: for every expert in the shape's row range
+// ceil(rows / tile rows) row tiles, each paired with every weight tile.  The list
+// is built on the device from the expert offsets (no host synchronisation).  Each
+// XCD takes a contiguous eighth of every segment's list, so consecutive entries
+// (same row tile, neighbouring weight tiles) share one L2; the segment with the
+// longer contraction is scheduled first.
 #include <limits.h>
 
 #include <type_traits>
@@ -39,27 +46,36 @@
 
 namespace moge {
 
-constexpr int kTileM = 256;        // rows per tile
-constexpr int kTileK = 64;         // contraction elements per stage
+constexpr int kTileK = 64;              // contraction elements per stage
 constexpr int kLineBytes = kTileK * 2;  // one operand row of a stage (bf16)
-constexpr int kABufs = 2;          // activation stages in LDS (loaded one stage ahead)
-constexpr int kBBufs = 3;          // weight stages in LDS (loaded two stages ahead)
-constexpr int kTileThreads = 256;  // 4 waves: 2 (rows) x 2 (weight rows)
+constexpr int kTileThreads = 256;       // 4 waves
 constexpr int kXcds = 8;
-constexpr int kAStageBytes = kTileM * kLineBytes;      // 32 KiB
-constexpr int kRowsPerLoad = 8;    // A rows one wave instruction moves
-constexpr int kFragBytes = 1024;   // one 16 x 32 bf16 MFMA fragment
+constexpr int kRowsPerLoad = 8;         // A rows one wave instruction moves
+constexpr int kFragBytes = 1024;        // one 16 x 32 bf16 MFMA fragment
 
-template <bool GATEUP> struct TileShape {
-  static constexpr int kWRows = GATEUP ? 192 : 256;    // weight rows per tile
-  static constexpr int kBStageBytes = kWRows * kLineBytes;   // kWRows / 8 fragments
-  static constexpr int kLdsBytes = kABufs * kAStageBytes + kBBufs * kBStageBytes;
-  static constexpr int kBlocksPerTile = kWRows / 32;   // 32-row weight blocks per tile
-  static constexpr int kWP = kBlocksPerTile / 2;       // ... per wave
+template <bool GATEUP, bool BIG> struct TileShape {
+  static constexpr int kM = BIG ? 256 : 64;                       // rows per tile
+  static constexpr int kWRows = BIG ? (GATEUP ? 192 : 256) : 128;  // weight rows per tile
+  static constexpr int kFeat = kWRows / 2;                         // gate/up features per tile
+  static constexpr int kWavesM = BIG ? 2 : 1;                      // waves along the rows
+  static constexpr int kWavesN = 4 / kWavesM;
+  static constexpr int kTP = kM / kWavesM / 32;                    // 32-row blocks per wave
+  static constexpr int kBlocksPerTile = kWRows / 32;               // 32-row weight blocks
+  static constexpr int kWP = kBlocksPerTile / kWavesN;             // ... per wave
+  static constexpr int kDA = BIG ? 2 : 6;                          // activation stages in LDS
+  static constexpr int kDB = BIG ? 3 : 6;                          // weight stages in LDS
+  static constexpr int kAStageBytes = kM * kLineBytes;
+  static constexpr int kBStageBytes = kWRows * kLineBytes;         // kWRows / 8 fragments
+  static constexpr int kLdsBytes = kDA * kAStageBytes + kDB * kBStageBytes;
   // wave instructions per stage: A (8 rows each), B (one fragment each)
-  static constexpr int kALoads = kTileM / kRowsPerLoad / 4;
+  static constexpr int kALoads = kM / kRowsPerLoad / 4;
   static constexpr int kBLoads = kBStageBytes / kFragBytes / 4;
-  static constexpr int kLoads = kALoads + kBLoads;
+  // one load after every kEvery MFMAs
+  static constexpr int kEvery = BIG ? (GATEUP ? 2 : 3) : 1;
+  static_assert(kDA <= kDB && (kDA == kDB || (kDA == 2 && kDB == 3)), "ring depths");
+  static_assert(kWP * kWavesN == kBlocksPerTile && kTP >= 1, "wave layout");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert((kALoads + kBLoads) * kEvery <= 4 * kTP * kWP, "loads must fit in a stage");
 };
 
 // One wave instruction: 64 lanes x 16 bytes from a buffer straight into LDS at
@@ -81,6 +97,17 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N < 64, "vmcnt field is 6 bits");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// the same for a wave-uniform n <= N
+template <int N> __device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N)
+      wait_vmcnt<N>();
+    else
+      wait_vmcnt_le<N - 1>(n);
+  }
+}
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 typedef __attribute__((address_space(3))) void* LdsPtr;
@@ -88,7 +115,9 @@ typedef __attribute__((address_space(3))) void* LdsPtr;
 // position of 16-byte chunk c of stage row r
 __device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// Row tiles of expert e of a segment (0 if it takes the streaming path).
+// Row tiles of kM rows of expert e of a segment (0 unless its row count is in the
+// range (thr, thr_hi] this tile shape serves).
+template <int kM>
 __device__ __forceinline__ int seg_expert_tiles(const TileSeg& g, int e, int* lo, int* cnt) {
   int l0, c;
   if (g.offsets) {
@@ -103,11 +132,12 @@ __device__ __forceinline__ int seg_expert_tiles(const TileSeg& g, int e, int* lo
   }
   *lo = l0;
   *cnt = c;
-  return c > g.thr ? (c + kTileM - 1) / kTileM : 0;
+  return (c > g.thr && c <= g.thr_hi) ? (c + kM - 1) / kM : 0;
 }
 
 // Find the row tile `mt` of a segment: expert, first row, rows.  Every lane of the
 // wave takes part (the prefix over experts is a wave scan).
+template <int kM>
 __device__ __forceinline__ bool seg_find_tile(const TileSeg& g, int mt, int* e_out, int* row0,
                                               int* rows) {
   const int l = threadIdx.x & 63;
@@ -115,7 +145,7 @@ __device__ __forceinline__ bool seg_find_tile(const TileSeg& g, int mt, int* e_o
   for (int e0 = 0; e0 < g.n_exp; e0 += 64) {
     const int e = e0 + l;
     int lo = 0, cnt = 0;
-    const int nt = e < g.n_exp ? seg_expert_tiles(g, e, &lo, &cnt) : 0;
+    const int nt = e < g.n_exp ? seg_expert_tiles<kM>(g, e, &lo, &cnt) : 0;
     // inclusive prefix of nt across the wave
     int inc = nt;
 #pragma unroll
@@ -134,8 +164,8 @@ __device__ __forceinline__ bool seg_find_tile(const TileSeg& g, int mt, int* e_o
       const int c_hit = __shfl(cnt, src, 64);
       const int j = mt - s_hit;
       *e_out = e_hit;
-      *row0 = lo_hit + j * kTileM;
-      *rows = min(kTileM, c_hit - j * kTileM);
+      *row0 = lo_hit + j * kM;
+      *rows = min(kM, c_hit - j * kM);
       return true;
     }
     base += __shfl(inc, 63, 64);
@@ -143,51 +173,56 @@ __device__ __forceinline__ bool seg_find_tile(const TileSeg& g, int mt, int* e_o
   return false;
 }
 
-__device__ __forceinline__ int seg_total_tiles(const TileSeg& g) {
+template <int kM> __device__ __forceinline__ int seg_total_tiles(const TileSeg& g) {
   const int l = threadIdx.x & 63;
   int s = 0;
   for (int e = l; e < g.n_exp; e += 64) {
     int lo, cnt;
-    s += seg_expert_tiles(g, e, &lo, &cnt);
+    s += seg_expert_tiles<kM>(g, e, &lo, &cnt);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
   return s;
 }
 
-template <bool GATEUP>
+template <bool GATEUP, bool BIG>
 __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
   typedef bf16 E;
-  typedef TileShape<GATEUP> S;
-  static_assert(S::kLdsBytes <= 160 * 1024, "LDS budget");
+  typedef TileShape<GATEUP, BIG> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::kLdsBytes];
-  // the tile descriptor lives in the last weight buffer, which the first loads
-  // (stages 0 and 1) leave alone and stage 2's loads overwrite only after the first
-  // barrier of the main loop
-  int* s_tile = reinterpret_cast<int*>(lds + kABufs * kAStageBytes + (kBBufs - 1) * S::kBStageBytes);
+  char* const ldsA = lds;
+  char* const ldsB = lds + S::kDA * S::kAStageBytes;
+  // the tile descriptor lives in the last weight buffer, which the loads issued
+  // before the main loop leave alone and later loads overwrite only after the
+  // main loop's first barrier
+  int* s_tile = reinterpret_cast<int*>(ldsB + (S::kDB - 1) * S::kBStageBytes);
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
-  // ---- which tile ------------------------------------------------------------
+  // ---- the tile lists (every wave computes the totals) -----------------------
+  const int nta = GATEUP ? a.inter / S::kFeat : d / S::kWRows;
+  const int ntb = b.n_exp ? (GATEUP ? b.inter / S::kFeat : d / S::kWRows) : 0;
+  const int ma = seg_total_tiles<S::kM>(a);
+  const int mb = b.n_exp ? seg_total_tiles<S::kM>(b) : 0;
+  // every XCD takes an equal share of each segment; the segment with the longer
+  // contraction (more work per tile) goes first, so its tiles do not pile up at
+  // the end
+  const bool b_first = (GATEUP ? d : b.inter) > (GATEUP ? d : a.inter);
+  const int tot0 = b_first ? mb * ntb : ma * nta, tot1 = b_first ? ma * nta : mb * ntb;
+  const int ch0 = (tot0 + kXcds - 1) / kXcds, ch1 = (tot1 + kXcds - 1) / kXcds;
+  // workgroup b runs on XCD b % 8 and takes that XCD's entry b / 8; the small shape
+  // (launched with at most one workgroup per CU) walks on to b / 8 + G, b / 8 + 2G,
+  // ... (G workgroups per XCD), so the CUs of an XCD work on neighbouring entries
+  const int x = blockIdx.x % kXcds;
+  auto run_tile = [&](int it) {
   if (w == 0) {
-    const int nta = GATEUP ? a.inter / (S::kWRows / 2) : d / S::kWRows;
-    const int ntb = b.n_exp ? (GATEUP ? b.inter / (S::kWRows / 2) : d / S::kWRows) : 0;
-    const int ma = seg_total_tiles(a);
-    const int mb = b.n_exp ? seg_total_tiles(b) : 0;
-    // every XCD takes an equal share of each segment; the segment with the longer
-    // contraction (more work per tile) goes first, so its tiles do not pile up at
-    // the end of the launch
-    const bool b_first = (GATEUP ? d : b.inter) > (GATEUP ? d : a.inter);
-    const int tot0 = b_first ? mb * ntb : ma * nta, tot1 = b_first ? ma * nta : mb * ntb;
-    const int ch0 = (tot0 + kXcds - 1) / kXcds, ch1 = (tot1 + kXcds - 1) / kXcds;
-    const int x = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
     int seg = -1, e = 0, row0 = 0, rows = 0, nt = 0;
     int which = -1, t = 0;
-    if (i < ch0) {
-      t = x * ch0 + i;
+    if (it < ch0) {
+      t = x * ch0 + it;
       if (t < tot0) which = 0;
-    } else if (i - ch0 < ch1) {
-      t = x * ch1 + (i - ch0);
+    } else {
+      t = x * ch1 + (it - ch0);
       if (t < tot1) which = 1;
     }
     if (which >= 0) {
@@ -195,7 +230,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       const TileSeg& g = seg ? b : a;
       const int ntg = seg ? ntb : nta;
       nt = t % ntg;
-      if (!seg_find_tile(g, t / ntg, &e, &row0, &rows) || rows <= 0) seg = -1;
+      if (!seg_find_tile<S::kM>(g, t / ntg, &e, &row0, &rows) || rows <= 0) seg = -1;
     }
     if (l == 0) {
       s_tile[0] = seg;
@@ -207,7 +242,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   }
   __syncthreads();
   const int seg = s_tile[0];
-  if (seg < 0) return;
+  if (seg >= 0) {
   const TileSeg g = seg == 0 ? a : b;
   const int e = s_tile[1];
   const int row0 = s_tile[2], rows = s_tile[3];
@@ -215,13 +250,13 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   const int K = GATEUP ? d : g.inter;              // contraction length of this segment
   const int nk = K / kTileK;                       // stages
 
-  // LDS byte address of the stage buffers; the wave index as a scalar (every load
-  // below has a wave-uniform destination)
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(LdsPtr)&lds[0]);
+  // LDS byte address of the buffers; the wave index as a scalar (every load below
+  // has a wave-uniform destination)
+  const uint32_t ldsA0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(LdsPtr)ldsA);
+  const uint32_t ldsB0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(LdsPtr)ldsB);
   const int wu = __builtin_amdgcn_readfirstlane(w);
   // the lane's row within an 8-row load and the chunk it fetches for that row
   const int lr = l >> 3;
-  auto load_chunk = [&](int row) { return swz_chunk(row, l & 7); };
 
   // ---- A: stage rows 8 * (kALoads * wave + i) + l / 8
   const Rsrc xr = make_rsrc(g.x, (uint64_t)g.x_rows * K * sizeof(E));
@@ -231,15 +266,15 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
     const int r = (wu * S::kALoads + i) * kRowsPerLoad + lr;
     const int rr = row0 + min(r, rows - 1);
     const int src = (GATEUP && g.row_src) ? g.row_src[rr] / g.row_div : rr;
-    a_voff[i] = (uint32_t)(((size_t)src * K + load_chunk(r) * 8) * sizeof(E));
+    a_voff[i] = (uint32_t)(((size_t)src * K + swz_chunk(r, l & 7) * 8) * sizeof(E));
   }
   // ---- B: the stage's weight rows in MFMA fragment order: fragment f = 2 rb + kh
   // holds rows 16 rb .. +15 and elements 32 kh .. +31 of the stage, lane j of the
   // fragment (16 bytes at 16 j) row j % 16, elements 8 (j / 16) .. +7.  This is the
   // packed weight layout's own tile format, so a packed fragment is one contiguous
   // 1 KiB read.  Row block rb is half rb % 2 of 32-row block rb / 2: for gate/up the
-  // gate (half 0) or up rows of features 96 nt + 16 (rb / 2) .. +15; for down,
-  // output columns 256 nt + 16 rb .. +15.
+  // gate (half 0) or up rows of features kFeat nt + 16 (rb / 2) .. +15; for down,
+  // output columns kWRows nt + 16 rb .. +15.
   const bool packed = g.packed != nullptr;
   Rsrc br0, br1;
   if (GATEUP) {
@@ -265,7 +300,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       const int pb = nt * S::kBlocksPerTile + blk;
       b_voff[i] = (uint32_t)((pb * nk * 4 + kh * 2 + half) * tb + l * 16);
     } else {
-      const int row = GATEUP ? nt * 96 + blk * 16 + (l & 15) : nt * 256 + rb * 16 + (l & 15);
+      const int row = GATEUP ? nt * S::kFeat + blk * 16 + (l & 15) : nt * S::kWRows + rb * 16 + (l & 15);
       b_voff[i] = (uint32_t)(((size_t)row * K + kh * 32 + (l >> 4) * 8) * sizeof(E));
     }
   }
@@ -278,28 +313,23 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   const uint32_t b_step = packed ? 4 * tb : kLineBytes;
   const uint32_t a_step = kLineBytes;
 
-  // wave load i of the A rows of stage kb, and of the B rows
-  auto issue_a = [&](int i, int kb) {
-    const uint32_t st = lds0 + (uint32_t)((kb % kABufs) * kAStageBytes);
-    lds_dma16(xr, a_voff[i], kb * a_step, st + (wu * S::kALoads + i) * kRowsPerLoad * kLineBytes);
+  // wave load i of the A rows of stage s, and of the B rows
+  auto issue_a = [&](int i, int s) {
+    const uint32_t st = ldsA0 + (uint32_t)((s % S::kDA) * S::kAStageBytes);
+    lds_dma16(xr, a_voff[i], s * a_step, st + (wu * S::kALoads + i) * kRowsPerLoad * kLineBytes);
   };
-  auto issue_b = [&](int i, int kb) {
-    const uint32_t st = lds0 + (uint32_t)(kABufs * kAStageBytes + (kb % kBBufs) * S::kBStageBytes);
-    lds_dma16(b_rsrc(i), b_voff[i], kb * b_step, st + (wu * S::kBLoads + i) * kFragBytes);
+  auto issue_b = [&](int i, int s) {
+    const uint32_t st = ldsB0 + (uint32_t)((s % S::kDB) * S::kBStageBytes);
+    lds_dma16(b_rsrc(i), b_voff[i], s * b_step, st + (wu * S::kBLoads + i) * kFragBytes);
   };
 
-  // ---- wave tile: 128 rows x (kWP * 32) weight rows as kTP x kWP 32x32 blocks.
+  // ---- wave tile: kTP 32-row blocks x kWP 32-weight-row blocks.
   // v_mfma_f32_32x32x16_bf16: lane l supplies row l % 32 of the weight block and
   // of the row block, contraction elements 8 (l / 32) .. +7 of the 16-element
   // sub-step; both operands use the same element assignment.
-  constexpr int kTP = 4, kWP = S::kWP;
+  constexpr int kTP = S::kTP, kWP = S::kWP;
   constexpr int kSub = kTileK / 16;                  // MFMA sub-steps per stage
-  // one load of the next stage after every kEvery MFMAs: the CU's memory path then
-  // works alongside the matrix cores, and the last loads still have the remaining
-  // MFMAs of the stage to land
-  constexpr int kEvery = GATEUP ? 2 : 3;
-  static_assert((S::kALoads + S::kBLoads) * kEvery <= kSub * kTP * kWP, "loads must fit in a stage");
-  const int wm = w & 1, wn = w >> 1;
+  const int wm = w % S::kWavesM, wn = w / S::kWavesM;
   f32x16 acc[kWP][kTP];
 #pragma unroll
   for (int q = 0; q < kWP; ++q)
@@ -325,14 +355,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       tf[p] = *reinterpret_cast<const bf16x8*>(A + (wm * kTP + p) * 32 * kLineBytes + off);
   };
 
-  // MFMAs of stage kb.  In between go out (every kEvery MFMAs, A first) the A
-  // loads of stage kb + 1 when `next_a`, and the B loads of stage kb + 2 when
-  // `next_b`.  Operand fragments are read one sub-step ahead.
+  // MFMAs of stage kb.  In between go out (one after every kEvery MFMAs, A first)
+  // the A loads of stage kb + kDA - 1 when `next_a`, and the B loads of stage
+  // kb + kDB - 1 when `next_b`.  Operand fragments are read one sub-step ahead.
   auto compute = [&](int kb, auto next_a, auto next_b) {
     constexpr int na = decltype(next_a)::value ? S::kALoads : 0;
     constexpr int nl = na + (decltype(next_b)::value ? S::kBLoads : 0);
-    const char* A = lds + (kb % kABufs) * kAStageBytes;
-    const char* B = lds + kABufs * kAStageBytes + (kb % kBBufs) * S::kBStageBytes;
+    const char* A = ldsA + (kb % S::kDA) * S::kAStageBytes;
+    const char* B = ldsB + (kb % S::kDB) * S::kBStageBytes;
     bf16x8 wf[2][kWP], tf[2][kTP];
     read_frags(A, B, 0, wf[0], tf[0]);
 #pragma unroll
@@ -344,55 +374,75 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
         for (int q = 0; q < kWP; ++q) {
           acc[q][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[h & 1][q], tf[h & 1][p], acc[q][p], 0, 0, 0);
           const int m = (h * kTP + p) * kWP + q;
-          const int j = m / kEvery;
-          if (m % kEvery == kEvery - 1 && j < nl) {
+          const int j = m / S::kEvery;
+          if (m % S::kEvery == S::kEvery - 1 && j < nl) {
             // keep the load where it is: the scheduler would otherwise bunch them
             __builtin_amdgcn_sched_barrier(0);
             if (j < na)
-              issue_a(j, kb + 1);
+              issue_a(j, kb + S::kDA - 1);
             else
-              issue_b(j - na, kb + 2);
+              issue_b(j - na, kb + S::kDB - 1);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
     }
   };
 
-  // Loads complete in issue order as far as vmcnt is concerned.  At the top of
-  // stage kb the youngest loads are stage kb + 1's B rows (kBLoads of them), issued
-  // after stage kb's A rows; everything older has to be in.
+  // Loads complete in issue order as far as vmcnt is concerned.  Before the loop
+  // go stages 0 .. kDB - 2 (A only up to kDA - 2), in stage order; the MFMAs of
+  // stage j then issue A of stage j + kDA - 1, then B of stage j + kDB - 1.  At
+  // the top of stage kb everything up to the last load stage kb needs has to be
+  // in; what may still be outstanding is
+  //   equal depths: the loads of stages kb+1 .. min(kb + kDA - 2, nk - 1);
+  //   depths 2, 3:  the B loads of stage kb + 1, if it exists.
+  auto pending = [&](int kb) {
+    if (S::kDA == S::kDB) return (S::kALoads + S::kBLoads) * max(0, min(S::kDA - 2, nk - 1 - kb));
+    return kb + 1 <= nk - 1 ? S::kBLoads : 0;
+  };
+  constexpr int kPendSteady = S::kDA == S::kDB ? (S::kDA - 2) * (S::kALoads + S::kBLoads) : S::kBLoads;
+
 #pragma unroll
-  for (int i = 0; i < S::kALoads; ++i) issue_a(i, 0);
+  for (int s = 0; s < S::kDB - 1; ++s) {
+    if (s < nk) {
+      if (s <= S::kDA - 2) {
 #pragma unroll
-  for (int i = 0; i < S::kBLoads; ++i) issue_b(i, 0);
-  if (nk > 1) {
+        for (int i = 0; i < S::kALoads; ++i) issue_a(i, s);
+      }
 #pragma unroll
-    for (int i = 0; i < S::kBLoads; ++i) issue_b(i, 1);
+      for (int i = 0; i < S::kBLoads; ++i) issue_b(i, s);
+    }
   }
-  for (int kb = 0; kb + 2 < nk; ++kb) {
-    wait_vmcnt<S::kBLoads>();
+  int kb = 0;
+  // both operands of a later stage go out
+  for (; kb + S::kDB - 1 < nk; ++kb) {
+    wait_vmcnt<kPendSteady>();
     // every wave's loads of stage kb are in, and every wave has finished reading
     // the buffers the loads issued during this stage overwrite (stage kb - 1's)
     barrier_only();
     compute(kb, std::true_type{}, std::true_type{});
   }
-  if (nk > 1) {
-    wait_vmcnt<S::kBLoads>();
+  // only activations of a later stage go out
+  for (; kb + S::kDA - 1 < nk; ++kb) {
+    wait_vmcnt_le<kPendSteady>(pending(kb));
     barrier_only();
-    compute(nk - 2, std::true_type{}, std::false_type{});
+    compute(kb, std::true_type{}, std::false_type{});
   }
-  wait_vmcnt<0>();
-  barrier_only();
-  compute(nk - 1, std::false_type{}, std::false_type{});
+  // nothing goes out
+  for (; kb < nk; ++kb) {
+    wait_vmcnt_le<kPendSteady>(pending(kb));
+    barrier_only();
+    compute(kb, std::false_type{}, std::false_type{});
+  }
 
   // ---- epilogue ----------------------------------------------------------------
-  // acc[q][p]: lane l, register r holds weight row 8*(r/4) + 4*(l/32) + r%4 of pair
-  // q for tile row 32*(4*wm + p) + l%32.  Gate/up pairs are (gate rows, up rows) of
-  // 16 features: registers r < 8 are gate, r + 8 the up value of the same feature.
+  // acc[q][p]: lane l, register r holds weight row 8*(r/4) + 4*(l/32) + r%4 of
+  // block q for tile row 32*(kTP*wm + p) + l%32.  Gate/up blocks are (gate rows, up
+  // rows) of 16 features: registers r < 8 are gate, r + 8 the up value of the same
+  // feature.
   E* out = static_cast<E*>(g.out);
 #pragma unroll
   for (int p = 0; p < kTP; ++p) {
-    const int r0 = wm * 128 + p * 32 + (l & 31);
+    const int r0 = (wm * kTP + p) * 32 + (l & 31);
     if (r0 >= rows) continue;
     const size_t orow = (size_t)(row0 + r0);
 #pragma unroll
@@ -418,38 +468,73 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       }
     }
   }
+  }  // seg >= 0
+  };
+  if constexpr (BIG) {
+    // one tile per workgroup: the big shape's registers are nearly all taken by the
+    // accumulators, and nothing may stay live across tiles
+    if ((int)(blockIdx.x / kXcds) < ch0 + ch1) run_tile(blockIdx.x / kXcds);
+  } else {
+    const int gx = gridDim.x / kXcds;
+    for (int it = blockIdx.x / kXcds; it < ch0 + ch1; it += gx) {
+      run_tile(it);
+      // every wave is done with this tile's LDS (and the descriptor) before the next
+      __syncthreads();
+    }
+  }
 }
 
 bool tile_path_ok(int d, int inter) {
-  return d % TileShape<false>::kWRows == 0 && d % kTileK == 0 && inter % kTileK == 0 &&
-         inter % (TileShape<true>::kWRows / 2) == 0;
+  // big tiles: 96-feature gate/up and 256-column down tiles; small tiles: 64 and
+  // 128 (implied); 64-element stages
+  return d % TileShape<false, true>::kWRows == 0 && d % kTileK == 0 && inter % kTileK == 0 &&
+         inter % TileShape<true, true>::kFeat == 0;
 }
 
-// Upper bound of a segment's row tiles, from host-known sizes only.
-static long long tile_bound(const TileSeg& g) {
+// Upper bound of a segment's row tiles of kM rows, from host-known sizes only.
+static long long tile_bound(const TileSeg& g, int kM) {
   if (g.n_exp == 0) return 0;
-  if (!g.offsets) return g.rows > g.thr ? (g.rows + kTileM - 1) / kTileM : 0;
+  if (!g.offsets) return (g.rows > g.thr && g.rows <= g.thr_hi) ? (g.rows + kM - 1) / kM : 0;
   const long long R = g.rows;
-  const long long big = R / (g.thr + 1);                    // experts above the threshold
-  return R / kTileM + (big < g.n_exp ? big : g.n_exp) + 1;
+  long long n_in = R / ((long long)g.thr + 1);              // experts above the threshold
+  if (n_in > g.n_exp) n_in = g.n_exp;
+  long long bound = R / kM + n_in + 1;
+  if (g.thr_hi < INT_MAX) {                                 // each at most ceil(thr_hi / kM) tiles
+    const long long b2 = n_in * ((g.thr_hi + kM - 1) / kM);
+    if (b2 < bound) bound = b2;
+  }
+  return bound;
 }
 
-hipError_t launch_ffn_tile(bool gateup, int d, const TileSeg& a, const TileSeg* b, hipStream_t st) {
+template <bool GATEUP, bool BIG>
+static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStream_t st) {
+  typedef TileShape<GATEUP, BIG> S;
   const TileSeg bb = b ? *b : TileSeg{};
-  const long long wa = gateup ? TileShape<true>::kWRows / 2 : TileShape<false>::kWRows;
-  const long long nta = gateup ? a.inter / wa : d / wa;
-  const long long ntb = b ? (gateup ? bb.inter / wa : d / wa) : 0;
+  const long long wa = GATEUP ? S::kFeat : S::kWRows;
+  const long long nta = GATEUP ? a.inter / wa : d / wa;
+  const long long ntb = b ? (GATEUP ? bb.inter / wa : d / wa) : 0;
   // each segment's tiles are spread over the XCDs separately
-  const long long ba = tile_bound(a) * nta, bbn = tile_bound(bb) * ntb;
-  const long long per_xcd = (ba + kXcds - 1) / kXcds + (bbn + kXcds - 1) / kXcds;
+  const long long ba = tile_bound(a, S::kM) * nta, bbn = tile_bound(bb, S::kM) * ntb;
+  long long per_xcd = (ba + kXcds - 1) / kXcds + (bbn + kXcds - 1) / kXcds;
   if (per_xcd == 0) return hipSuccess;
+  if (!BIG) {
+    // at most one workgroup per CU (the LDS rings take most of a CU's LDS), each
+    // walking its XCD's share of the list: the bound counts every expert that
+    // could fall in the range, and a launch that finds none stays cheap
+    const long long slots = device_cus() / kXcds;
+    if (per_xcd > slots) per_xcd = slots > 0 ? slots : 1;
+  }
   const long long grid = per_xcd * kXcds;
   if (grid > INT_MAX) return hipErrorInvalidValue;
-  if (gateup)
-    hipLaunchKernelGGL(k_ffn_tile<true>, dim3((unsigned)grid), dim3(kTileThreads), 0, st, a, bb, d);
-  else
-    hipLaunchKernelGGL(k_ffn_tile<false>, dim3((unsigned)grid), dim3(kTileThreads), 0, st, a, bb, d);
+  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG>), dim3((unsigned)grid), dim3(kTileThreads), 0, st,
+                     a, bb, d);
   return hipGetLastError();
+}
+
+hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const TileSeg* b,
+                           hipStream_t st) {
+  if (gateup) return big ? launch_shape<true, true>(d, a, b, st) : launch_shape<true, false>(d, a, b, st);
+  return big ? launch_shape<false, true>(d, a, b, st) : launch_shape<false, false>(d, a, b, st);
 }
 
 }  // namespace moge
