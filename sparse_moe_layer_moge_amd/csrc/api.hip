@@ -183,11 +183,11 @@ moge::TileSeg tile_view(const moge::FfnSeg& f, bool gateup) {
 }
 
 // Both projections of up to two segments.  The streaming kernels take routed
-// experts with at most kStreamMaxRows rows (the shared segment up to
-// kSharedStreamMaxRows), the 64-row tile kernels those with up to
-// kSmallTileMaxRows, the 256-row tile kernels the rest.  A tile launch is made only
-// when some expert can fall in its range (an expert never has more rows than the
-// batch has tokens).
+// experts with at most kStreamMaxRows rows, the 64-row tile kernels those with up
+// to kSmallTileMaxRows, the 256-row tile kernels the rest; the shared segment has
+// its own limits (kSharedStreamMaxRows, kSharedSmallGateUpRows, kSharedSmallDownRows).  A tile launch is
+// made only when some expert can fall in its range (an expert never has more rows
+// than the batch has tokens).
 moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh,
                       hipStream_t st, bool marks) {
   // the tile path covers bf16 and its tile shapes; everything else streams
@@ -199,11 +199,13 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
   routed.thr = thr;
   if (sh) sh->thr = sh_thr;
   const bool sh_stream = sh && sh->rows <= sh_thr;
-  // tile launches: `lo < rows <= hi`
-  struct Range { bool on; int lo, hi; bool big; };
-  const Range ranges[2] = {{tiles_ok && T > thr, thr, thr_big, false},
-                           {tiles_ok && T > thr_big, thr_big, INT_MAX, true}};
+  // tile launches: routed experts with lo < rows <= hi, the shared segment with
+  // sh_lo < rows <= sh_hi
+  struct Range { int lo, hi, sh_lo, sh_hi; bool big; };
   for (int gateup = 1; gateup >= 0; --gateup) {
+    const int sh_big = gateup ? moge::kSharedSmallGateUpRows : moge::kSharedSmallDownRows;
+    const Range ranges[2] = {{thr, thr_big, sh_thr, sh_big, false},
+                             {thr_big, INT_MAX, sh_big, INT_MAX, true}};
     if (gateup)
       CHECK(hip_check(moge::launch_ffn_gateup(dtype, d, routed, sh_stream ? sh : nullptr, st),
                       "expert gate/up"));
@@ -211,16 +213,18 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
       CHECK(hip_check(moge::launch_ffn_down(dtype, d, routed, sh_stream ? sh : nullptr, st),
                       "expert down"));
     for (const Range& rg : ranges) {
-      if (!rg.on) continue;
+      const bool routed_here = tiles_ok && T > rg.lo;
+      const bool sh_here = tiles_ok && sh && sh->rows > rg.sh_lo && sh->rows <= rg.sh_hi;
+      if (!routed_here && !sh_here) continue;
       moge::TileSeg a = tile_view(routed, gateup);
       a.thr = rg.lo;
       a.thr_hi = rg.hi;
-      const bool sh_here = sh && !sh_stream && sh->rows > rg.lo && sh->rows <= rg.hi;
+      if (!routed_here) a.n_exp = 0;
       moge::TileSeg b;
       if (sh_here) {
         b = tile_view(*sh, gateup);
-        b.thr = rg.lo;
-        b.thr_hi = rg.hi;
+        b.thr = rg.sh_lo;
+        b.thr_hi = rg.sh_hi;
       }
       CHECK(hip_check(moge::launch_ffn_tile(gateup, rg.big, d, a, sh_here ? &b : nullptr, st),
                       gateup ? "expert gate/up tiles" : "expert down tiles"));

@@ -65,11 +65,16 @@ hipError_t launch_ffn_down(int dtype, int d, const FfnSeg& a, const FfnSeg* b, h
 // Routed experts with at most kStreamMaxRows rows take the streaming kernels; those
 // with more take 64-row MFMA tiles up to kSmallTileMaxRows rows and 256-row tiles
 // beyond.  The shared experts (one segment of T rows) stream up to
-// kSharedStreamMaxRows: at small T their few weight tiles would leave most CUs idle,
-// while in the streaming launch they share the CUs with the routed experts.
+// kSharedStreamMaxRows and take 64-row tiles up to kSharedSmallGateUpRows (gate/up)
+// or kSharedSmallDownRows (down): a single segment of a few hundred rows has too
+// few 256-row tiles to fill the CUs (the down projection, with 256 output columns
+// per tile, far fewer than gate/up), while in the launch of the routed experts it
+// shares them.  The limits are measured choices on MI355X.
 constexpr int kStreamMaxRows = 32;
 constexpr int kSharedStreamMaxRows = 64;
 constexpr int kSmallTileMaxRows = 128;
+constexpr int kSharedSmallGateUpRows = 128;
+constexpr int kSharedSmallDownRows = 512;
 struct TileSeg {
   const void* x = nullptr;         // activation rows (x, or H for the down projection)
   int x_rows = 0;
