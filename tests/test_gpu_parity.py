@@ -145,6 +145,47 @@ def test_expert_ffn(lib, name, T):
     assert err <= tolerance(cfg), err
 
 
+# Per-expert row counts on both sides of every switch between the kernels: the
+# streaming kernels (up to 32 rows), 64-row tiles (up to 128) and 256-row tiles,
+# with partial tiles of every kind.  The oracle checks sampled rows of every expert.
+BOUNDARY_ROWS = [0, 1, 16, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 513]
+
+
+def test_expert_ffn_row_count_boundaries(lib):
+    import torch
+    cfg = C1
+    rows = list(BOUNDARY_ROWS)
+    rows += [0] * (cfg.N - len(rows))
+    rows[-1] = (-sum(rows)) % cfg.K            # total divisible by K
+    counts = np.array(rows, dtype=np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    T = R // cfg.K
+    inp, dw = layer_inputs(cfg, 64)            # weights only
+    x_perm_h = S.make_x(cfg, T=R, seed=7)
+    dims = dims_of(lib, cfg, T)
+    y_perm = _empty((R, cfg.d), dw["x"].dtype)
+    ws = _empty(lib.workspace_size(dims), torch.uint8)
+    say("expert_ffn boundaries", R)
+    lib.expert_ffn(dims, to_dev(x_perm_h, cfg.dtype), to_dev(offsets, "f32"),
+                   dw["w_gate"], dw["w_up"], dw["w_down"], y_perm, ws)
+    torch.cuda.synchronize()
+    y = values(to_host(y_perm))
+    # sampled rows of every expert: first, last, and two inside
+    pick, sub_counts = [], []
+    for e in range(cfg.N):
+        lo, c = int(offsets[e]), int(counts[e])
+        sel = sorted({lo + j for j in (0, c // 3, (2 * c) // 3, c - 1) if 0 <= j < c})
+        pick += sel
+        sub_counts.append(len(sel))
+    pick = np.array(pick, dtype=np.int64)
+    sub_off = np.concatenate([[0], np.cumsum(sub_counts)]).astype(np.int64)
+    ref = O.expert_ffn(O.to_f64(x_perm_h[pick], cfg.dtype), sub_off, inp.w_gate, inp.w_up,
+                       inp.w_down, cfg.dtype)
+    err = normwise_rel_err(y[pick], ref)
+    assert err <= tolerance(cfg), err
+
+
 @pytest.mark.parametrize("name,T", [("C0", 64), ("C1", 64), ("C1", 100)])
 def test_shared_expert_via_expert_ffn(lib, name, T):
     import torch
@@ -216,7 +257,11 @@ def _sample(T):
 
 
 @pytest.mark.parametrize("name,T", [("C0", 64), ("C1", 64), ("C2", 456), ("C3", 4096),
-                                    ("C4", 16384), ("C0", 1), ("C0", 65), ("C1", 17)])
+                                    ("C4", 16384), ("C0", 1), ("C0", 65), ("C1", 17),
+                                    # the shared segment's switches: streaming up to 64
+                                    # rows, 64-row tiles up to 128 (gate/up) / 512 (down)
+                                    ("C1", 65), ("C1", 128), ("C1", 129), ("C1", 512),
+                                    ("C1", 513)])
 def test_layer_on_given_scores(lib, name, T):
     cfg = CONFIGS[name]
     inp, dw = layer_inputs(cfg, T)
