@@ -147,8 +147,8 @@ __device__ __forceinline__ void stream_blocks(const Rsrc (&wr)[NB], const uint32
 // bf16 variant fits 3 waves per SIMD; float fragments are twice as wide.
 template <typename E, int MS> struct StreamDepth { static constexpr int value = 8; };
 template <> struct StreamDepth<bf16, 2> { static constexpr int value = 5; };
-template <> struct StreamDepth<bf16, 3> { static constexpr int value = 4; };
-template <> struct StreamDepth<bf16, 4> { static constexpr int value = 3; };
+template <> struct StreamDepth<bf16, 3> { static constexpr int value = 5; };
+template <> struct StreamDepth<bf16, 4> { static constexpr int value = 4; };
 template <> struct StreamDepth<float, 1> { static constexpr int value = 4; };
 template <> struct StreamDepth<float, 2> { static constexpr int value = 2; };
 template <> struct StreamDepth<float, 3> { static constexpr int value = 2; };
