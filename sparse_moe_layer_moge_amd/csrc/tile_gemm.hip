@@ -439,34 +439,42 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   // block q for tile row 32*(kTP*wm + p) + l%32.  Gate/up blocks are (gate rows, up
   // rows) of 16 features: registers r < 8 are gate, r + 8 the up value of the same
   // feature.
+  // The tile goes through LDS (the stage rings are free now), so that the global
+  // stores are whole rows of 16-byte chunks instead of 8-byte pieces of 32 rows per
+  // instruction.  An LDS row holds kNCp chunk slots (kNC used); chunk c of tile row
+  // r sits at slot c ^ (r % kNCp), which keeps the scattered writes free of bank
+  // conflicts.  Gate/up first applies SwiGLU in registers.
   E* out = static_cast<E*>(g.out);
+  constexpr int kOutCols = GATEUP ? S::kFeat : S::kWRows;   // output columns per tile
+  constexpr int kNC = kOutCols * (int)sizeof(E) / 16;        // 16-byte chunks per row
+  constexpr int kNCp = kNC <= 8 ? 8 : kNC <= 16 ? 16 : 32;   // ... rounded up to 2^k
+  constexpr int kPitch = kNCp * 16;
+  constexpr int kCPB = GATEUP ? 2 : 4;                       // chunks per 32-row block
+  static_assert(kNC <= kNCp && S::kM * kPitch <= S::kLdsBytes, "the output tile fits in LDS");
+  __syncthreads();   // every wave has finished reading the last stage
 #pragma unroll
   for (int p = 0; p < kTP; ++p) {
-    const int r0 = (wm * kTP + p) * 32 + (l & 31);
-    if (r0 >= rows) continue;
-    const size_t orow = (size_t)(row0 + r0);
+    const int r = (wm * kTP + p) * 32 + (l & 31);
 #pragma unroll
     for (int q = 0; q < kWP; ++q) {
-      if (GATEUP) {
-        const int fbase = (nt * S::kBlocksPerTile + wn * kWP + q) * 16 + 4 * (l >> 5);
 #pragma unroll
-        for (int gq = 0; gq < 2; ++gq) {
-          f32x4 hv;
+      for (int gq = 0; gq < kCPB; ++gq) {
+        f32x4 v;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) hv[k] = silu(acc[q][p][gq * 4 + k]) * acc[q][p][gq * 4 + k + 8];
-          store4(out + orow * g.inter + fbase + 8 * gq, hv);
-        }
-      } else {
-        const int cbase = (nt * S::kBlocksPerTile + wn * kWP + q) * 32 + 4 * (l >> 5);
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          f32x4 v;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) v[k] = acc[q][p][gq * 4 + k];
-          store4(out + orow * d + cbase + 8 * gq, v);
-        }
+        for (int k = 0; k < 4; ++k)
+          v[k] = GATEUP ? silu(acc[q][p][gq * 4 + k]) * acc[q][p][gq * 4 + k + 8] : acc[q][p][gq * 4 + k];
+        const int c = (wn * kWP + q) * kCPB + gq;
+        store4(reinterpret_cast<E*>(lds + r * kPitch + ((c ^ (r & (kNCp - 1))) << 4) + 8 * (l >> 5)), v);
       }
     }
+  }
+  __syncthreads();
+  const int ld = GATEUP ? g.inter : d;
+  const int col0 = nt * kOutCols;
+  for (int i = tid; i < rows * kNC; i += kTileThreads) {
+    const int r = i / kNC, c = i - r * kNC;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * kPitch + ((c ^ (r & (kNCp - 1))) << 4));
+    *reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * ld + col0 + c * 8) = v;
   }
   }  // seg >= 0
   };
