@@ -280,6 +280,34 @@ def test_layer_on_given_scores(lib, name, T):
     assert err <= tolerance(cfg), err
 
 
+# Small bf16 layers that reach code paths the full-size workloads do not:
+#  SB1: shapes the tile kernels do not cover (widths not a multiple of 96), so the
+#       streaming kernels take every expert, in several 64-row passes;
+#  SB2: tile shapes with contractions shorter than the LDS rings (gate/up 4
+#       stages of 64, down 3 routed and 6 shared), at batch sizes that send the
+#       experts to the streaming kernels (T=16), to 64-row tiles (T=300: about 75
+#       rows per expert; the 300-row shared segment takes 256-row tiles for gate/up
+#       and 64-row tiles for down) and to 256-row tiles (T=1200).
+SB1 = replace(C0, name="SB1-bf16-streaming-only", dtype="bf16")
+SB2 = replace(C0, name="SB2-bf16-short-contractions", dtype="bf16", inter=192, shared_inter=384)
+
+
+@pytest.mark.parametrize("cfg,T", [(SB1, 300), (SB2, 16), (SB2, 300), (SB2, 1200)])
+def test_small_bf16_layers(lib, cfg, T):
+    inp, dw = layer_inputs(cfg, T)
+    scores = S.make_scores(cfg, T=T)
+    say("small bf16 layer", cfg.name, T)
+    out = _run_layer(lib, cfg, T, dw, logits_in=scores)
+    r = O.route(scores, cfg.M, cfg.kp)
+    np.testing.assert_array_equal(out["idx"], r["idx"])
+    tok = _sample(T)
+    ref = O.layer(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down,
+                  inp.ws_gate, inp.ws_up, inp.ws_down, M=cfg.M, kp=cfg.kp, dtype=cfg.dtype,
+                  logits_f32=scores, tokens=tok)
+    err = normwise_rel_err(values(out["y"])[tok], ref["y"])
+    assert err <= tolerance(cfg), err
+
+
 def _score_error_bound(inp, cfg):
     """Bound on |float32 scores - exact scores| for any summation order:
     (d + 2) * 2^-24 * sum_j |x_j w_j| (+ one rounding of the bias add)."""
