@@ -39,7 +39,10 @@
  *     moge_workspace_size() -> MOGE_ERR_WORKSPACE; a failed kernel launch ->
  *     MOGE_ERR_HIP. In every error case nothing has been enqueued. T = 0 returns
  *     MOGE_OK and enqueues nothing.
- *   - Limits: N <= 256, K = M*K' <= 64, d, I and I_s multiples of 32, T*K < 2^31.
+ *   - Limits: N <= 256, K = M*K' <= 64, d, I and I_s multiples of 32, T*K < 2^31,
+ *     and under 4 GiB each: every activation buffer ([T*K, d], [T*K, I], [T, I_s])
+ *     and one expert's gate and up weights together (2*I*d elements; 2*I_s*d for
+ *     the shared experts), which the kernels address with 32-bit offsets.
  *   - Results are deterministic: repeated calls on the same inputs give identical
  *     bits (no floating-point atomics; integer histogram counts only).
  *

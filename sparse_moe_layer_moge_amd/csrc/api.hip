@@ -76,7 +76,9 @@ moge_status_t check_dims(const moge_dims_t* d) {
   long long widest = R * d->d;
   if (R * d->inter > widest) widest = R * d->inter;
   if ((long long)d->T * d->shared_inter > widest) widest = (long long)d->T * d->shared_inter;
-  if ((long long)d->inter * d->d > widest) widest = (long long)d->inter * d->d;
+  // one expert's packed gate/up pair, and the shared experts' (one buffer each)
+  if (2ll * d->inter * d->d > widest) widest = 2ll * d->inter * d->d;
+  if (2ll * d->shared_inter * d->d > widest) widest = 2ll * d->shared_inter * d->d;
   if (widest * es > 0xFFFFFFFFll)
     return fail(MOGE_ERR_UNSUPPORTED, "an activation or expert buffer exceeds 4 GiB (%lld bytes)",
                 widest * es);

@@ -56,6 +56,11 @@ def route(d, logits=FAKE, probs=None, idx=FAKE, gate=FAKE):
     (dict(d=5100), 2, "multiples of 32"),
     (dict(inter=1000), 2, "multiples of 32"),
     (dict(shared_inter=100), 2, "multiples of 32"),
+    # buffers addressed with 32-bit offsets: activations, one expert's packed gate/up
+    # pair (2 * inter * d), the shared experts' gate/up pair
+    (dict(T=1 << 20), 2, "exceeds 4 GiB"),
+    (dict(d=32768, inter=40960, shared_inter=0), 2, "exceeds 4 GiB"),
+    (dict(d=32768, inter=64, shared_inter=40960), 2, "exceeds 4 GiB"),
 ])
 def test_invalid_dims(kw, status, msg):
     assert route(dims(**kw)) == status
