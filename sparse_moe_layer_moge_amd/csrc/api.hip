@@ -116,7 +116,7 @@ Plan make_plan(const moge_dims_t* d) {
   Plan p{};
   const size_t T = d->T, N = d->N, M = d->M, K = (size_t)d->M * d->k_per_group, R = T * K;
   const size_t es = esize(d), nblk = moge::perm_blocks(d->T);
-  p.ksplit = moge::router_ksplit(d->T, d->d, d->N);
+  p.ksplit = moge::router_ksplit(d->dtype, d->T, d->d, d->N);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;

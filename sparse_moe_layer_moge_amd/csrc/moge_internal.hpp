@@ -15,7 +15,7 @@ hipError_t launch_router_scores(int dtype, const void* x, const void* w_router, 
 hipError_t launch_route(const float* partial, int ksplit, int T, int N, int M, int kp,
                         const float* bias, float* logits_out, float* probs, int32_t* idx,
                         float* gate, hipStream_t st);
-int router_ksplit(int T, int d, int N);
+int router_ksplit(int dtype, int T, int d, int N);
 
 // ---- permutation (permute.hip) ---------------------------------------------
 constexpr int kPermTokens = 64;  // tokens per permutation block (one wave)
