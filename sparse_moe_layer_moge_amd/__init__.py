@@ -170,7 +170,8 @@ def layer_forward(dims: Dims, x, w_router, router_bias, w_gate, w_up, w_down, ws
 
 
 def set_stage_events(events) -> None:
-    """events: a sequence of STAGE_EVENTS raw hipEvent_t handles (ints), or None."""
+    """events: a sequence of STAGE_EVENTS raw hipEvent_t handles (ints; None skips
+    that point), or None to stop recording."""
     if events is None:
         _check(lib.moge_set_stage_events(None, 0), "moge_set_stage_events")
         return

@@ -19,7 +19,7 @@ thread_local hipEvent_t g_stage_events[MOGE_STAGE_EVENTS];
 thread_local bool g_record_stages = false;
 
 void mark(int i, hipStream_t st) {
-  if (g_record_stages) (void)hipEventRecord(g_stage_events[i], st);
+  if (g_record_stages && g_stage_events[i]) (void)hipEventRecord(g_stage_events[i], st);
 }
 
 moge_status_t fail(moge_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -352,10 +352,7 @@ moge_status_t moge_set_stage_events(void* const* events, int32_t n_events) {
   }
   if (n_events != MOGE_STAGE_EVENTS)
     return fail(MOGE_ERR_INVALID_ARG, "n_events=%d, expected %d", n_events, MOGE_STAGE_EVENTS);
-  for (int i = 0; i < MOGE_STAGE_EVENTS; ++i) {
-    if (!events[i]) return fail(MOGE_ERR_INVALID_ARG, "events[%d] is NULL", i);
-    g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
-  }
+  for (int i = 0; i < MOGE_STAGE_EVENTS; ++i) g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
   g_record_stages = true;
   return ok();
 }
