@@ -38,8 +38,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_F32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-FFN_SOURCES = [os.path.join(ROOT, "sparse_moe_layer_moge_amd", "csrc", f)
-               for f in ("ffn.hip", "stream_tile.hpp", "packed_layout.hpp", "moge_common.hpp")]
+CSRC = os.path.join(ROOT, "sparse_moe_layer_moge_amd", "csrc")
+# sources of the kernels behind the roofline line (a stored traffic figure is used
+# only while they are unchanged)
+FFN_SOURCES = {"bf16": ("ffn.hip", "ffn_rows.hpp", "stream_tile.hpp", "packed_layout.hpp",
+                        "tile_gemm.hip", "moge_common.hpp"),
+               "w8": ("ffn_w8.hip", "ffn_rows.hpp", "w8_layout.hpp", "moge_common.hpp")}
 
 
 def parse_args():
@@ -55,15 +59,18 @@ def parse_args():
     ap.add_argument("--row-major", action="store_true",
                     help="time moge_layer_forward on the row-major weights instead of "
                          "moge_layer_forward_packed")
+    ap.add_argument("--w8", action="store_true",
+                    help="time moge_layer_forward_w8: int8 expert weights with per-channel "
+                         "scales (synthetic codes), bf16 activations")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the CPU oracle sample (default: the whole batch, max 64)")
     return ap.parse_args()
 
 
-def ffn_source_hash() -> str:
+def ffn_source_hash(kind: str = "bf16") -> str:
     h = hashlib.sha256()
-    for f in FFN_SOURCES:
-        with open(f, "rb") as fh:
+    for f in FFN_SOURCES[kind]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -92,27 +99,34 @@ class Hip:
         self.rt.hipEventDestroy(e)
 
 
-def algorithmic_work(cfg, counts):
+def algorithmic_work(cfg, counts, w8: bool = False):
     """Bytes and flops the method itself needs (intermediates not counted).
 
     Expert weights are counted once for every expert that receives at least one
     row, plus the shared and router weights, x in and y out.  Flops count the
-    router, routed and shared matmuls (2 per multiply-add)."""
+    router, routed and shared matmuls (2 per multiply-add).  With int8 expert
+    weights a weight is one byte, plus one float32 scale per weight row."""
     es = 2 if cfg.dtype == "bf16" else 4
     d, I, Is, T, N = cfg.d, cfg.inter, cfg.I_s, cfg.T, cfg.N
     R = T * cfg.K
     active = int((counts > 0).sum())
-    gate_up = dict(bytes=active * 2 * d * I * es + 2 * d * Is * es + T * d * es + (R * I + T * Is) * es,
+    if w8:
+        gu_w, dn_w = 2 * d * I + 2 * I * 4, d * I + d * 4             # one routed expert
+        sgu_w, sdn_w = 2 * d * Is + 2 * Is * 4, d * Is + (d * 4 if Is else 0)
+    else:
+        gu_w, dn_w, sgu_w, sdn_w = 2 * d * I * es, d * I * es, 2 * d * Is * es, d * Is * es
+    gate_up = dict(bytes=active * gu_w + sgu_w + T * d * es + (R * I + T * Is) * es,
                    flops=4 * R * d * I + 4 * T * d * Is)
-    down = dict(bytes=active * d * I * es + d * Is * es + (R * I + T * Is) * es + (R + T) * d * es,
+    down = dict(bytes=active * dn_w + sdn_w + (R * I + T * Is) * es + (R + T) * d * es,
                 flops=2 * R * d * I + 2 * T * d * Is)
-    layer = dict(bytes=active * 3 * d * I * es + 3 * d * Is * es + N * d * es + 2 * T * d * es,
+    layer = dict(bytes=active * (gu_w + dn_w) + sgu_w + sdn_w + N * d * es + 2 * T * d * es,
                  flops=2 * T * d * N + 6 * R * d * I + 6 * T * d * Is)
     return dict(gate_up=gate_up, down=down, layer=layer, active_experts=active)
 
 
-def cpu_baseline(cfg, inp, n_tokens: int, min_seconds: float = 10.0):
-    """Time the CPU oracle (numpy float64) on the first n_tokens tokens' outputs."""
+def cpu_baseline(cfg, inp, n_tokens: int, min_seconds: float = 10.0, w8=None):
+    """Time the CPU oracle (numpy float64) on the first n_tokens tokens' outputs
+    (the int8-weight layer when w8 holds codes and scales)."""
     import numpy as np
     from oracle import moge_oracle as O
     try:
@@ -124,9 +138,15 @@ def cpu_baseline(cfg, inp, n_tokens: int, min_seconds: float = 10.0):
     reps = 0
     t0 = time.perf_counter()
     while True:   # repeat the same call until about 10 s of CPU work (at most 30 calls)
-        O.layer(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down,
-                inp.ws_gate, inp.ws_up, inp.ws_down, M=cfg.M, kp=cfg.kp, dtype=cfg.dtype,
-                tokens=tok)
+        if w8 is None:
+            O.layer(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down,
+                    inp.ws_gate, inp.ws_up, inp.ws_down, M=cfg.M, kp=cfg.kp, dtype=cfg.dtype,
+                    tokens=tok)
+        else:
+            O.layer_w8(inp.x, inp.w_router, inp.router_bias, w8["q_gate"], w8["s_gate"],
+                       w8["q_up"], w8["s_up"], w8["q_down"], w8["s_down"], w8["qs_gate"],
+                       w8["ss_gate"], w8["qs_up"], w8["ss_up"], w8["qs_down"], w8["ss_down"],
+                       M=cfg.M, kp=cfg.kp, dtype=cfg.dtype, tokens=tok)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or reps >= 30:
@@ -176,14 +196,30 @@ def main() -> int:
     idx = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda")
     gc = torch.empty((cfg.M,), dtype=torch.int32, device="cuda")
     # weights are parameters: packed once, outside the timed region
-    packed = torch.empty(moge.packed_weights_size(dims), dtype=torch.uint8, device="cuda")
-    moge.pack_weights(dims, w["w_gate"], w["w_up"], w["w_down"], w["ws_gate"], w["ws_up"],
-                      w["ws_down"], packed)
+    w8_host = None
+    if args.w8:
+        if cfg.dtype != "bf16":
+            print(json.dumps({"error": "int8 expert weights take bf16 activations"}))
+            return 2
+        w8_host = S.make_w8_weights(cfg)
+        q = {k: dev(v) for k, v in w8_host.items()}
+        packed = torch.empty(moge.w8_weights_size(dims), dtype=torch.uint8, device="cuda")
+        moge.pack_weights_w8(dims, q["q_gate"], q["q_up"], q["q_down"], q["s_gate"], q["s_up"],
+                             q["s_down"], q["qs_gate"], q["qs_up"], q["qs_down"], q["ss_gate"],
+                             q["ss_up"], q["ss_down"], packed)
+        del q
+    else:
+        packed = torch.empty(moge.packed_weights_size(dims), dtype=torch.uint8, device="cuda")
+        moge.pack_weights(dims, w["w_gate"], w["w_up"], w["w_down"], w["ws_gate"], w["ws_up"],
+                          w["ws_down"], packed)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
     def step():
-        if args.row_major:
+        if args.w8:
+            moge.layer_forward_w8(dims, x, w["w_router"], w["router_bias"], packed, y, ws,
+                                  topk_idx_out=idx, group_counts_out=gc)
+        elif args.row_major:
             moge.layer_forward(dims, x, w["w_router"], w["router_bias"], w["w_gate"], w["w_up"],
                                w["w_down"], w["ws_gate"], w["ws_up"], w["ws_down"], y, ws,
                                topk_idx_out=idx, group_counts_out=gc)
@@ -241,7 +277,8 @@ def main() -> int:
     mean_stage = stage_ms.mean(axis=0)
     counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=cfg.N)
     gcounts = gc.cpu().numpy()
-    work = algorithmic_work(cfg, counts)
+    work = algorithmic_work(cfg, counts, w8=args.w8)
+    workload = cfg.name + ("-w8a16" if args.w8 else "")
 
     ms_per_step = 1e3 * elapsed / K
     value = cfg.T * K / elapsed
@@ -259,8 +296,8 @@ def main() -> int:
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
-            tr = json.load(f).get(f"gate_up@{cfg.name}")
-        if tr and tr.get("source_hash") == ffn_source_hash():
+            tr = json.load(f).get(f"gate_up@{workload}")
+        if tr and tr.get("source_hash") == ffn_source_hash("w8" if args.w8 else "bf16"):
             traffic = tr["bytes_per_launch"]
     except (OSError, ValueError):
         pass
@@ -270,10 +307,11 @@ def main() -> int:
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic (seeded N(0,std) inputs, random-init weights)",
-        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "N": cfg.N, "M": cfg.M,
+        "config": {"workload": workload, "T": cfg.T, "d": cfg.d, "N": cfg.N, "M": cfg.M,
                    "k_per_group": cfg.kp, "inter": cfg.inter, "shared_experts": cfg.n_shared,
                    "shared_inter_total": cfg.I_s, "parallelism": "single GPU",
-                   "weights": "row-major" if args.row_major else "packed"},
+                   "weights": ("int8 codes, float32 per-row scales" if args.w8 else
+                               "row-major" if args.row_major else "packed")},
         "roofline": {"bound": bound, "kernel": "gate_up+SwiGLU (routed+shared)",
                      "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -293,7 +331,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         n = args.cpu_tokens if args.cpu_tokens > 0 else min(cfg.T, 64)
-        rec["cpu_baseline"] = cpu_baseline(cfg, inp, n)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, n, w8=w8_host)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

@@ -204,6 +204,73 @@ moge_status_t moge_layer_forward_packed(const moge_dims_t* dims, const void* x,
                                         float* topk_gate_out, int32_t* group_counts_out,
                                         void* ws, size_t ws_bytes, void* stream);
 
+/* Weight-only int8 experts (W8A16).  Quantised deployment of the experts is part
+ * of the inference work on the TechWalker page (section 三 推理性能优化, expert-aware
+ * quantisation); the CSDN page reports W8A8 within 1.2% of full accuracy.  This is
+ * the weight half: every row of W_gate, W_up, W_down and of the shared experts'
+ * weights holds int8 codes q with one float32 scale s, weight = s * q; activations,
+ * H and the outputs stay bf16.  At decode batch sizes the layer streams its expert
+ * weights from HBM, so one byte per weight halves the dominant stream.  Every
+ * expert takes the streaming kernels whatever its row count: the int8 layer is
+ * meant for decode batches (up to about 64 rows per expert); prefill belongs to
+ * the bf16 packed layer.
+ * Requirements: dtype MOGE_BF16; d, inter and shared_inter multiples of 64
+ * (MOGE_ERR_UNSUPPORTED otherwise).
+ *
+ * Buffer layout (each region starts at a 256-byte boundary):
+ *   code tiles: routed gate/up parts of experts 0..N-1, routed down parts, shared
+ *     gate/up part, shared down part;
+ *   scales (float32): gate [N,I], up [N,I], down [N,d], shared gate [I_s],
+ *     shared up [I_s], shared down [d].
+ * Code tile = 16 rows x 64 contraction elements (1 KiB) stored as 64 chunks of 16
+ * consecutive elements; chunk l holds row l % 16, elements 16*(l/16) ..
+ * 16*(l/16)+15.  Gate/up part of an expert: for row block b < I/16 and step
+ * s < d/64, the gate tile then the up tile of rows 16b..16b+15 at tile index
+ * (b*(d/64) + s)*2 + {0,1}.  Down part: for row block b < d/32 and step s < I/64,
+ * the tiles of rows 32b..32b+15 and 32b+16..32b+31 at tile index
+ * (b*(I/64) + s)*2 + {0,1}. */
+
+/* Bytes of the int8 expert-weight buffer for these dims; 0 if the dims are invalid
+ * or outside the requirements above. */
+size_t moge_w8_weights_size(const moge_dims_t* dims);
+
+/* Build the int8 buffer from codes and scales the caller already has (a pure copy;
+ * asynchronous on `stream`).  All device pointers:
+ *   q_gate, q_up [N,I,d], q_down [N,d,I] int8 (16-byte aligned),
+ *   s_gate, s_up [N,I], s_down [N,d] float32,
+ *   qs_gate, qs_up [I_s,d], qs_down [d,I_s] int8, ss_gate, ss_up [I_s], ss_down [d]
+ *     float32 (may be NULL only when shared_inter == 0),
+ *   w8: 256-byte aligned, >= moge_w8_weights_size bytes, caller-owned. */
+moge_status_t moge_pack_weights_w8(const moge_dims_t* dims, const int8_t* q_gate,
+                                   const int8_t* q_up, const int8_t* q_down, const float* s_gate,
+                                   const float* s_up, const float* s_down, const int8_t* qs_gate,
+                                   const int8_t* qs_up, const int8_t* qs_down,
+                                   const float* ss_gate, const float* ss_up,
+                                   const float* ss_down, void* w8, size_t w8_bytes,
+                                   void* stream);
+
+/* Quantise the six row-major bf16 weight tensors (shapes as moge_layer_forward,
+ * 16-byte aligned) into the int8 buffer, symmetric per output row:
+ *   s = max_k |w[k]| / 127, q[k] = rint(w[k] / s) with ties to even, clamped to
+ *   [-127, 127]; every step in float32 (IEEE division); a row of zeros gets s = 0,
+ *   q = 0.  Weights must be finite.  Asynchronous on `stream`. */
+moge_status_t moge_quantize_weights_w8(const moge_dims_t* dims, const void* w_gate,
+                                       const void* w_up, const void* w_down, const void* ws_gate,
+                                       const void* ws_up, const void* ws_down, void* w8,
+                                       size_t w8_bytes, void* stream);
+
+/* moge_layer_forward with the expert weights taken from an int8 buffer (other
+ * arguments and the workspace as moge_layer_forward).  Routing, permutation and
+ * combine are the same kernels; the experts compute, per output channel,
+ * s * (sum_k a[k] * q[k]) in float32 from bf16 activations a, then SwiGLU and the
+ * bf16 roundings of the bf16 layer. */
+moge_status_t moge_layer_forward_w8(const moge_dims_t* dims, const void* x, const void* w_router,
+                                    const float* router_bias, const void* w8,
+                                    const float* logits_in, void* y, float* logits_out,
+                                    int32_t* topk_idx_out, float* topk_gate_out,
+                                    int32_t* group_counts_out, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* Stage timing for profiling.  events: MOGE_STAGE_EVENTS hipEvent_t handles
  * (passed as void*) created by the caller; moge_layer_forward then records
  * events[0] before its first kernel and events[i] after stage i on its stream:
@@ -212,7 +279,8 @@ moge_status_t moge_layer_forward_packed(const moge_dims_t* dims, const void* x,
  * A NULL entry skips that point (each recorded event costs a few microseconds of
  * GPU time).  events == NULL or n_events == 0 turns recording off.  The setting
  * belongs to the calling thread.  Any other n_events -> MOGE_ERR_INVALID_ARG.
- * Both moge_layer_forward and moge_layer_forward_packed record them. */
+ * moge_layer_forward, moge_layer_forward_packed and moge_layer_forward_w8 record
+ * them. */
 #define MOGE_STAGE_EVENTS 7
 moge_status_t moge_set_stage_events(void* const* events, int32_t n_events);
 

@@ -13,6 +13,9 @@ Sources (cited by page title and section, never by line):
   [RC]   Reportify concept page "分组混合专家模型", bullet list 技术创新细节.
   [MK]   mokono.cn, "盘古Pro MoE", 核心亮点 item 1 (分组专家机制): 8 groups of 8,
          one expert per group, 4 shared experts kept.
+  [TW3]  TechWalker page, section 三 (推理性能优化) - quantised deployment of the
+         experts (expert-aware quantisation).
+  [CS]   CSDN page (hwcomputing.csdn.net) - W8A8 deployment within 1.2% accuracy.
 
 What the pages fix (restated):
   * The N routed experts are split evenly into M groups of G = N/M experts; each
@@ -37,6 +40,10 @@ Readings where the pages are silent (each listed in the design notes as well):
   R9 imbalance score = (max_g load_g - min_g load_g) / T, load_g = number of
      (token, expert) assignments that land in group g.
   R10 y[t] = shared(x_t) + sum_k gate[t,k] * FFN_{idx[t,k]}(x_t), k in slot order.
+  Q1 int8 expert weights (the weight half of [CS]'s W8A8): symmetric, one float32
+     scale per output row, s = max|w| / 127, q = rint(w / s) ties to even, clamped
+     to [-127, 127], each step in float32; a zero row gets s = 0, q = 0.  The layer
+     then uses the weights s * q exactly; activations stay as they are.
 
 Parity pins: see the oracle tests (brute force, closed forms, invariants, special
 cases).  Every function here is pinned by at least one of them.
@@ -54,7 +61,10 @@ import numpy as np
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     """Exact float64 value of a layer tensor: float32 arrays are widened; bf16
-    tensors arrive as uint16 bit patterns = the high half of a float32 word."""
+    tensors arrive as uint16 bit patterns = the high half of a float32 word;
+    "f64" values (dequantised int8 weights) are taken as they are."""
+    if dtype == "f64":
+        return np.asarray(a, dtype=np.float64)
     if dtype == "bf16":
         bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
@@ -240,7 +250,8 @@ def combine(y_perm64: np.ndarray, pair_row: np.ndarray, gate: np.ndarray,
 
 def layer(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
           M: int, kp: int, dtype: str, logits_f32: Optional[np.ndarray] = None,
-          tokens: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+          tokens: Optional[np.ndarray] = None,
+          wdtype: Optional[str] = None) -> Dict[str, np.ndarray]:
     """MoGE layer forward: scores -> global softmax -> per-group top-K' ->
     expert-contiguous permutation -> routed SwiGLU experts -> shared experts ->
     gate-weighted combine.
@@ -248,7 +259,10 @@ def layer(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_dow
     logits_f32: router scores to route on; when None they are computed here from
     x and w_router in float64 and rounded to float32 for the selection (R1).
     tokens: optional subset of token indices; routing covers all T tokens, the
-    permutation / FFN / combine only the listed ones (rows of y follow `tokens`)."""
+    permutation / FFN / combine only the listed ones (rows of y follow `tokens`).
+    wdtype: dtype of the expert and shared weights when it differs from the
+    activations' ("f64" for dequantised int8 weights); the router uses `dtype`."""
+    wdtype = dtype if wdtype is None else wdtype
     x = np.asarray(x)
     T = x.shape[0]
     N = w_gate.shape[0]
@@ -271,9 +285,62 @@ def layer(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_dow
     x_sel = to_f64(x[tok], dtype)
     token_of_row = sub["sorted_pair"].astype(np.int64) // K
     x_perm = x_sel[token_of_row]
-    y_perm = expert_ffn(x_perm, sub["offsets"], w_gate, w_up, w_down, dtype)
-    sh = shared_experts(x_sel, ws_gate, ws_up, ws_down, dtype)
+    y_perm = expert_ffn(x_perm, sub["offsets"], w_gate, w_up, w_down, wdtype)
+    sh = shared_experts(x_sel, ws_gate, ws_up, ws_down, wdtype)
     out["shared"] = sh
     out["y"] = combine(y_perm, sub["pair_row"], r["gate"][tok], sh, len(tok), K)
     out["tokens"] = tok
     return out
+
+
+# ----------------------------------------------------------------------------
+# Weight-only int8 expert weights (Q1; [TW3], [CS])
+# ----------------------------------------------------------------------------
+
+W8_QMAX = 127
+
+
+def w8_quantize(w, dtype: str):
+    """int8 codes q[..., rows, K] and float32 scales s[..., rows] of weights w
+    (rows along the second-to-last axis, the contraction along the last).
+
+    s = fl32(max_k |w[k]| / 127); q[k] = rint(fl32(w[k] / s)), ties to even,
+    clamped to [-127, 127]; a row of zeros gets s = 0 and q = 0 (Q1)."""
+    w32 = to_f64(w, dtype).astype(np.float32)           # exact for bf16 and float32
+    absmax = np.max(np.abs(w32), axis=-1)
+    s = (absmax / np.float32(W8_QMAX)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.rint(w32 / s[..., None])                  # float32 division, then ties-to-even
+    q = np.where(s[..., None] > 0, np.clip(r, -W8_QMAX, W8_QMAX), 0).astype(np.int8)
+    return q, s
+
+
+class W8Weights:
+    """The float64 weights s[..., r] * q[..., r, k] of int8 codes, widened one
+    leading index (one expert) at a time when indexed, or whole via np.asarray."""
+
+    def __init__(self, q: np.ndarray, s: np.ndarray):
+        self.q = np.asarray(q, dtype=np.int8)
+        self.s = np.asarray(s, dtype=np.float32)
+        if self.s.shape != self.q.shape[:-1]:
+            raise ValueError("one scale per row of codes")
+        self.shape = self.q.shape
+
+    def __getitem__(self, e):
+        return self.q[e].astype(np.float64) * self.s[e].astype(np.float64)[..., None]
+
+    def __array__(self, dtype=None, copy=None):
+        a = self.q.astype(np.float64) * self.s.astype(np.float64)[..., None]
+        return a if dtype is None else a.astype(dtype)
+
+
+def layer_w8(x, w_router, router_bias, q_gate, s_gate, q_up, s_up, q_down, s_down,
+             qs_gate, ss_gate, qs_up, ss_up, qs_down, ss_down, M: int, kp: int,
+             dtype: str = "bf16", logits_f32: Optional[np.ndarray] = None,
+             tokens: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """The MoGE layer with int8 expert and shared weights: `layer` on the weights
+    s * q (Q1).  The activations and the router keep `dtype`."""
+    return layer(x, w_router, router_bias, W8Weights(q_gate, s_gate), W8Weights(q_up, s_up),
+                 W8Weights(q_down, s_down), W8Weights(qs_gate, ss_gate),
+                 W8Weights(qs_up, ss_up), W8Weights(qs_down, ss_down), M=M, kp=kp,
+                 dtype=dtype, logits_f32=logits_f32, tokens=tokens, wdtype="f64")

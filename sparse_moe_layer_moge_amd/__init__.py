@@ -70,6 +70,13 @@ _SIGS = {
                                          ctypes.c_size_t, _P]),
     "moge_layer_forward_packed": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P,
                                                  _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moge_w8_weights_size": (ctypes.c_size_t, [ctypes.POINTER(Dims)]),
+    "moge_pack_weights_w8": (ctypes.c_int, [ctypes.POINTER(Dims)] + [_P] * 13
+                             + [ctypes.c_size_t, _P]),
+    "moge_quantize_weights_w8": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P,
+                                                ctypes.c_size_t, _P]),
+    "moge_layer_forward_w8": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, ctypes.c_size_t, _P]),
 }
 STAGE_EVENTS = 7
 STAGE_NAMES = ("router_scores", "route", "permute", "gate_up", "down", "combine")
@@ -96,7 +103,7 @@ def header_functions(path: str = HEADER):
     with open(path) as f:
         text = f.read()
     decls = [ln for ln in text.splitlines() if not ln.lstrip().startswith(("*", "/*", "//"))]
-    return sorted(set(m for ln in decls for m in re.findall(r"\b(moge_[a-z_]+)\(", ln)))
+    return sorted(set(m for ln in decls for m in re.findall(r"\b(moge_[a-z0-9_]+)\(", ln)))
 
 
 lib = load_library()
@@ -200,3 +207,37 @@ def layer_forward_packed(dims: Dims, x, w_router, router_bias, packed, y, ws, lo
                                          _ptr(topk_gate_out), _ptr(group_counts_out), _ptr(ws),
                                          ws.numel() * ws.element_size(), _stream(stream)),
            "moge_layer_forward_packed")
+
+
+def w8_weights_size(dims: Dims) -> int:
+    return int(lib.moge_w8_weights_size(ctypes.byref(dims)))
+
+
+def pack_weights_w8(dims: Dims, q_gate, q_up, q_down, s_gate, s_up, s_down, qs_gate, qs_up,
+                    qs_down, ss_gate, ss_up, ss_down, w8, stream=None) -> None:
+    _check(lib.moge_pack_weights_w8(ctypes.byref(dims), _ptr(q_gate), _ptr(q_up), _ptr(q_down),
+                                    _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(qs_gate),
+                                    _ptr(qs_up), _ptr(qs_down), _ptr(ss_gate), _ptr(ss_up),
+                                    _ptr(ss_down), _ptr(w8), w8.numel() * w8.element_size(),
+                                    _stream(stream)),
+           "moge_pack_weights_w8")
+
+
+def quantize_weights_w8(dims: Dims, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w8,
+                        stream=None) -> None:
+    _check(lib.moge_quantize_weights_w8(ctypes.byref(dims), _ptr(w_gate), _ptr(w_up),
+                                        _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
+                                        _ptr(w8), w8.numel() * w8.element_size(),
+                                        _stream(stream)),
+           "moge_quantize_weights_w8")
+
+
+def layer_forward_w8(dims: Dims, x, w_router, router_bias, w8, y, ws, logits_in=None,
+                     logits_out=None, topk_idx_out=None, topk_gate_out=None,
+                     group_counts_out=None, stream=None) -> None:
+    _check(lib.moge_layer_forward_w8(ctypes.byref(dims), _ptr(x), _ptr(w_router),
+                                     _ptr(router_bias), _ptr(w8), _ptr(logits_in), _ptr(y),
+                                     _ptr(logits_out), _ptr(topk_idx_out), _ptr(topk_gate_out),
+                                     _ptr(group_counts_out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)),
+           "moge_layer_forward_w8")

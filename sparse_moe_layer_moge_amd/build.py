@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libmoge.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "router.hip", "permute.hip", "ffn.hip", "combine.hip", "pack.hip", "tile_gemm.hip"]
+SOURCES = ["api.hip", "router.hip", "permute.hip", "ffn.hip", "ffn_w8.hip", "combine.hip", "pack.hip",
+           "tile_gemm.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

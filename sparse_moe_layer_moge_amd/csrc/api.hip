@@ -11,6 +11,7 @@
 #include "../../include/moge.h"
 #include "moge_internal.hpp"
 #include "packed_layout.hpp"
+#include "w8_layout.hpp"
 
 namespace {
 
@@ -100,6 +101,20 @@ moge_status_t check_ptr(const void* p, size_t align, const char* name, bool requ
     const moge_status_t s_ = (expr);        \
     if (s_ != MOGE_OK) return s_;           \
   } while (0)
+
+// The int8 experts: bf16 activations, and contraction widths made of whole
+// 64-element code tiles.
+moge_status_t check_w8_dims(const moge_dims_t* d) {
+  CHECK(check_dims(d));
+  if (d->dtype != MOGE_BF16)
+    return fail(MOGE_ERR_UNSUPPORTED, "int8 expert weights take bf16 activations (dtype=%d)",
+                d->dtype);
+  if (d->d % 64 || d->inter % 64 || d->shared_inter % 64)
+    return fail(MOGE_ERR_UNSUPPORTED,
+                "int8 experts need d=%d, inter=%d and shared_inter=%d to be multiples of 64", d->d,
+                d->inter, d->shared_inter);
+  return MOGE_OK;
+}
 
 // ---------------------------------------------------------------------------
 // workspace layout (256-byte aligned regions)
@@ -236,11 +251,27 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
   return MOGE_OK;
 }
 
+// Weight-only int8 experts: every expert streams its codes whatever its row count
+// (the MFMA tile kernels take bf16 weights only).
+moge_status_t run_ffn_w8(int d, moge::FfnSeg& routed, moge::FfnSeg* sh, hipStream_t st,
+                         bool marks) {
+  routed.thr = INT_MAX;
+  if (sh) sh->thr = INT_MAX;
+  CHECK(hip_check(moge::launch_ffn_gateup_w8(d, routed, sh, st), "int8 expert gate/up"));
+  if (marks) mark(4, st);
+  CHECK(hip_check(moge::launch_ffn_down_w8(d, routed, sh, st), "int8 expert down"));
+  if (marks) mark(5, st);
+  return MOGE_OK;
+}
+
 struct Weights {
   const void *gate = nullptr, *up = nullptr, *down = nullptr;        // row-major routed
   const void *s_gate = nullptr, *s_up = nullptr, *s_down = nullptr;  // row-major shared
   const void *p_gu = nullptr, *p_down = nullptr;                     // packed routed
   const void *ps_gu = nullptr, *ps_down = nullptr;                   // packed shared
+  bool w8 = false;  // p_* / ps_* hold int8 code tiles with the scales below
+  const float *sc_gate = nullptr, *sc_up = nullptr, *sc_down = nullptr;     // routed
+  const float *ssc_gate = nullptr, *ssc_up = nullptr, *ssc_down = nullptr;  // shared
 };
 
 // The whole layer on one stream; `w` holds either row-major or packed weights
@@ -313,6 +344,9 @@ moge_status_t layer_impl(const moge_dims_t* dims, const void* x, const void* w_r
   routed.w_down = w.down;
   routed.p_gu = w.p_gu;
   routed.p_down = w.p_down;
+  routed.sc_gate = w.sc_gate;
+  routed.sc_up = w.sc_up;
+  routed.sc_down = w.sc_down;
   routed.h = at<char>(ws, p.h);
   routed.y = at<char>(ws, p.y_perm);
   moge::FfnSeg sh;
@@ -327,10 +361,16 @@ moge_status_t layer_impl(const moge_dims_t* dims, const void* x, const void* w_r
     sh.w_down = w.s_down;
     sh.p_gu = w.ps_gu;
     sh.p_down = w.ps_down;
+    sh.sc_gate = w.ssc_gate;
+    sh.sc_up = w.ssc_up;
+    sh.sc_down = w.ssc_down;
     sh.h = at<char>(ws, p.hs);
     sh.y = at<char>(ws, p.sh);
   }
-  CHECK(run_ffn(dims->dtype, dims->d, T, routed, shared ? &sh : nullptr, st, true));
+  if (w.w8)
+    CHECK(run_ffn_w8(dims->d, routed, shared ? &sh : nullptr, st, true));
+  else
+    CHECK(run_ffn(dims->dtype, dims->d, T, routed, shared ? &sh : nullptr, st, true));
   // S7 combine
   CHECK(hip_check(moge::launch_combine(dims->dtype, T, K, dims->d, routed.y, pair_row, gate,
                                        shared ? sh.y : nullptr, y, st),
@@ -545,6 +585,131 @@ moge_status_t moge_layer_forward_packed(const moge_dims_t* dims, const void* x,
   if (dims->shared_inter > 0) {
     w.ps_gu = base + pp.shared_gu;
     w.ps_down = base + pp.shared_down;
+  }
+  return layer_impl(dims, x, w_router, router_bias, w, logits_in, y, logits_out, topk_idx_out,
+                    topk_gate_out, group_counts_out, ws, ws_bytes, stream);
+}
+
+size_t moge_w8_weights_size(const moge_dims_t* dims) {
+  const std::string saved = g_last_error;
+  const moge_status_t s = check_w8_dims(dims);
+  g_last_error = saved;
+  if (s != MOGE_OK) return 0;
+  return moge::w8_parts(dims->d, dims->N, dims->inter, dims->shared_inter).total;
+}
+
+moge_status_t moge_pack_weights_w8(const moge_dims_t* dims, const int8_t* q_gate,
+                                   const int8_t* q_up, const int8_t* q_down, const float* s_gate,
+                                   const float* s_up, const float* s_down, const int8_t* qs_gate,
+                                   const int8_t* qs_up, const int8_t* qs_down,
+                                   const float* ss_gate, const float* ss_up,
+                                   const float* ss_down, void* w8, size_t w8_bytes,
+                                   void* stream) {
+  CHECK(check_w8_dims(dims));
+  const bool shared = dims->shared_inter > 0;
+  CHECK(check_ptr(q_gate, 16, "q_gate", true));
+  CHECK(check_ptr(q_up, 16, "q_up", true));
+  CHECK(check_ptr(q_down, 16, "q_down", true));
+  CHECK(check_ptr(s_gate, 4, "s_gate", true));
+  CHECK(check_ptr(s_up, 4, "s_up", true));
+  CHECK(check_ptr(s_down, 4, "s_down", true));
+  CHECK(check_ptr(qs_gate, 16, "qs_gate", shared));
+  CHECK(check_ptr(qs_up, 16, "qs_up", shared));
+  CHECK(check_ptr(qs_down, 16, "qs_down", shared));
+  CHECK(check_ptr(ss_gate, 4, "ss_gate", shared));
+  CHECK(check_ptr(ss_up, 4, "ss_up", shared));
+  CHECK(check_ptr(ss_down, 4, "ss_down", shared));
+  CHECK(check_ptr(w8, 256, "w8", true));
+  const int d = dims->d, N = dims->N, I = dims->inter, Is = dims->shared_inter;
+  const moge::W8Parts wp = moge::w8_parts(d, N, I, Is);
+  if (w8_bytes < wp.total)
+    return fail(MOGE_ERR_INVALID_ARG, "w8 buffer has %zu bytes, need %zu", w8_bytes, wp.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int8_t* dst = static_cast<int8_t*>(w8);
+  auto copy = [&](size_t off, const float* src, size_t n, const char* what) {
+    return hip_check(hipMemcpyAsync(dst + off, src, n * 4, hipMemcpyDeviceToDevice, st), what);
+  };
+  CHECK(hip_check(moge::launch_w8_pack(q_gate, q_up, N, I, d, dst + wp.routed_gu, st),
+                  "pack int8 routed gate/up"));
+  CHECK(hip_check(moge::launch_w8_pack(q_down, nullptr, N, d, I, dst + wp.routed_down, st),
+                  "pack int8 routed down"));
+  CHECK(copy(wp.s_gate, s_gate, (size_t)N * I, "copy gate scales"));
+  CHECK(copy(wp.s_up, s_up, (size_t)N * I, "copy up scales"));
+  CHECK(copy(wp.s_down, s_down, (size_t)N * d, "copy down scales"));
+  if (shared) {
+    CHECK(hip_check(moge::launch_w8_pack(qs_gate, qs_up, 1, Is, d, dst + wp.shared_gu, st),
+                    "pack int8 shared gate/up"));
+    CHECK(hip_check(moge::launch_w8_pack(qs_down, nullptr, 1, d, Is, dst + wp.shared_down, st),
+                    "pack int8 shared down"));
+    CHECK(copy(wp.ss_gate, ss_gate, (size_t)Is, "copy shared gate scales"));
+    CHECK(copy(wp.ss_up, ss_up, (size_t)Is, "copy shared up scales"));
+    CHECK(copy(wp.ss_down, ss_down, (size_t)d, "copy shared down scales"));
+  }
+  return ok();
+}
+
+moge_status_t moge_quantize_weights_w8(const moge_dims_t* dims, const void* w_gate,
+                                       const void* w_up, const void* w_down, const void* ws_gate,
+                                       const void* ws_up, const void* ws_down, void* w8,
+                                       size_t w8_bytes, void* stream) {
+  CHECK(check_w8_dims(dims));
+  const bool shared = dims->shared_inter > 0;
+  CHECK(check_ptr(w_gate, 16, "w_gate", true));
+  CHECK(check_ptr(w_up, 16, "w_up", true));
+  CHECK(check_ptr(w_down, 16, "w_down", true));
+  CHECK(check_ptr(ws_gate, 16, "ws_gate", shared));
+  CHECK(check_ptr(ws_up, 16, "ws_up", shared));
+  CHECK(check_ptr(ws_down, 16, "ws_down", shared));
+  CHECK(check_ptr(w8, 256, "w8", true));
+  const int d = dims->d, N = dims->N, I = dims->inter, Is = dims->shared_inter;
+  const moge::W8Parts wp = moge::w8_parts(d, N, I, Is);
+  if (w8_bytes < wp.total)
+    return fail(MOGE_ERR_INVALID_ARG, "w8 buffer has %zu bytes, need %zu", w8_bytes, wp.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(w8);
+  int8_t* dst = reinterpret_cast<int8_t*>(base);
+  auto sc = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  CHECK(hip_check(moge::launch_w8_quantize(w_gate, w_up, N, I, d, dst + wp.routed_gu,
+                                           sc(wp.s_gate), sc(wp.s_up), st),
+                  "quantize routed gate/up"));
+  CHECK(hip_check(moge::launch_w8_quantize(w_down, nullptr, N, d, I, dst + wp.routed_down,
+                                           sc(wp.s_down), nullptr, st),
+                  "quantize routed down"));
+  if (shared) {
+    CHECK(hip_check(moge::launch_w8_quantize(ws_gate, ws_up, 1, Is, d, dst + wp.shared_gu,
+                                             sc(wp.ss_gate), sc(wp.ss_up), st),
+                    "quantize shared gate/up"));
+    CHECK(hip_check(moge::launch_w8_quantize(ws_down, nullptr, 1, d, Is, dst + wp.shared_down,
+                                             sc(wp.ss_down), nullptr, st),
+                    "quantize shared down"));
+  }
+  return ok();
+}
+
+moge_status_t moge_layer_forward_w8(const moge_dims_t* dims, const void* x, const void* w_router,
+                                    const float* router_bias, const void* w8,
+                                    const float* logits_in, void* y, float* logits_out,
+                                    int32_t* topk_idx_out, float* topk_gate_out,
+                                    int32_t* group_counts_out, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  CHECK(check_w8_dims(dims));
+  CHECK(check_ptr(w8, 256, "w8", true));
+  const moge::W8Parts wp = moge::w8_parts(dims->d, dims->N, dims->inter, dims->shared_inter);
+  const char* base = static_cast<const char*>(w8);
+  auto sc = [&](size_t off) { return reinterpret_cast<const float*>(base + off); };
+  Weights w;
+  w.w8 = true;
+  w.p_gu = base + wp.routed_gu;
+  w.p_down = base + wp.routed_down;
+  w.sc_gate = sc(wp.s_gate);
+  w.sc_up = sc(wp.s_up);
+  w.sc_down = sc(wp.s_down);
+  if (dims->shared_inter > 0) {
+    w.ps_gu = base + wp.shared_gu;
+    w.ps_down = base + wp.shared_down;
+    w.ssc_gate = sc(wp.ss_gate);
+    w.ssc_up = sc(wp.ss_up);
+    w.ssc_down = sc(wp.ss_down);
   }
   return layer_impl(dims, x, w_router, router_bias, w, logits_in, y, logits_out, topk_idx_out,
                     topk_gate_out, group_counts_out, ws, ws_bytes, stream);

@@ -14,32 +14,12 @@
 #include <math.h>
 
 #include "moge_common.hpp"
+#include "ffn_rows.hpp"
 #include "moge_internal.hpp"
 #include "packed_layout.hpp"
 #include "stream_tile.hpp"
 
 namespace moge {
-
-struct SegView {
-  int lo, cnt;
-};
-
-// rows of expert e; offsets from the caller are clamped into [0, rows]
-__device__ __forceinline__ SegView expert_rows(const FfnSeg& g, int e) {
-  SegView v;
-  if (g.offsets) {
-    int lo = g.offsets[e], hi = g.offsets[e + 1];
-    lo = max(0, min(lo, g.rows));
-    hi = max(lo, min(hi, g.rows));
-    v.lo = lo;
-    v.cnt = hi - lo;
-  } else {
-    v.lo = 0;
-    v.cnt = g.rows;
-  }
-  if (v.cnt > g.thr) v.cnt = 0;   // the tile path's expert
-  return v;
-}
 
 // Every block accumulates its K steps in the same order (no rotation: measured,
 // rotating the start step did not change the achieved bandwidth), so results do
@@ -233,10 +213,13 @@ static int stream_slots() { return 3 * 4 * device_cus(); }
 // whose item size (k blocks) is closest to an even share of the launch's weight
 // bytes over one round of resident waves.  Segments whose rows need more than one
 // 16-row subtile run slower per byte, so they aim at half the share.
-static int blocks_per_wave(int blocks_per_expert, double block_bytes, double share) {
+static int blocks_per_wave(int blocks_per_expert, double block_bytes, double share,
+                           int multiple) {
+  // a multiple of `multiple` when the expert's block count allows one
+  if (blocks_per_expert % multiple) multiple = 1;
   int best = 1;
   double best_err = 1e300;
-  for (int k = 1; k <= 8; ++k) {
+  for (int k = multiple; k <= 8; k += multiple) {
     if (blocks_per_expert % k) continue;
     const double err = fabs(k * block_bytes - share);
     if (err < best_err) {
@@ -250,12 +233,15 @@ static int blocks_per_wave(int blocks_per_expert, double block_bytes, double sha
 // rows that a segment's experts may hold: > 16 means more than one row subtile
 static bool wide_rows(const FfnSeg& g) { return g.offsets == nullptr && g.rows > 16; }
 
-static void plan_blocks(FfnSeg& a, FfnSeg* b, double a_block, double b_block, int a_bpe,
-                        int b_bpe) {
+void plan_blocks(FfnSeg& a, FfnSeg* b, double a_block, double b_block, int a_bpe, int b_bpe,
+                 int multiple) {
   const double total = a_block * a.n_exp * a_bpe + (b ? b_block * b->n_exp * b_bpe : 0.0);
   const double share = total / stream_slots();
-  a.nblk = blocks_per_wave(a_bpe, a_block, wide_rows(a) ? share / 2 : share);
-  if (b) b->nblk = blocks_per_wave(b_bpe, b_block, wide_rows(*b) ? share / 2 : share);
+  a.nblk = wide_rows(a) ? blocks_per_wave(a_bpe, a_block, share / 2, 1)
+                        : blocks_per_wave(a_bpe, a_block, share, multiple);
+  if (b)
+    b->nblk = wide_rows(*b) ? blocks_per_wave(b_bpe, b_block, share / 2, 1)
+                            : blocks_per_wave(b_bpe, b_block, share, multiple);
 }
 
 hipError_t launch_ffn_gateup(int dtype, int d, const FfnSeg& a0, const FfnSeg* b0, hipStream_t st) {

@@ -51,6 +51,9 @@ struct FfnSeg {
   const void* w_down = nullptr;  // [n_exp, d, inter]
   const void* p_gu = nullptr;    // packed gate/up parts, expert-strided (packed_layout.hpp)
   const void* p_down = nullptr;  // packed down parts, expert-strided
+  const float* sc_gate = nullptr;  // int8 experts: per-channel scales of the gate rows
+  const float* sc_up = nullptr;    //   [n_exp, inter], of the up rows [n_exp, inter]
+  const float* sc_down = nullptr;  //   and of the down rows [n_exp, d] (w8_layout.hpp)
   int nblk = 1;                  // row blocks per wave (set by the launcher)
   int thr = 0x7fffffff;          // experts with more rows than this are left to the tile path
   void* h = nullptr;             // [rows, inter] dtype (gate/up output, down input)
@@ -60,6 +63,26 @@ struct FfnSeg {
 hipError_t launch_ffn_gateup(int dtype, int d, const FfnSeg& a, const FfnSeg* b, hipStream_t st);
 // down projection for up to two segments in one launch
 hipError_t launch_ffn_down(int dtype, int d, const FfnSeg& a, const FfnSeg* b, hipStream_t st);
+// Row blocks per wave (a.nblk, b->nblk) for a streaming launch: *_block = weight
+// bytes of one row block, *_bpe = row blocks per expert; a segment of experts
+// with at most 16 rows gets a multiple of `multiple` blocks where the block count
+// per expert allows it.
+void plan_blocks(FfnSeg& a, FfnSeg* b, double a_block, double b_block, int a_bpe, int b_bpe,
+                 int multiple = 1);
+
+// ---- weight-only int8 expert FFN (ffn_w8.hip, bf16 activations) ------------
+// Same segments, with p_gu / p_down holding int8 codes (w8_layout.hpp) and the
+// sc_* scales set; every expert streams, whatever its row count.  Needs d, inter
+// multiples of 64.
+hipError_t launch_ffn_gateup_w8(int d, const FfnSeg& a, const FfnSeg* b, hipStream_t st);
+hipError_t launch_ffn_down_w8(int d, const FfnSeg& a, const FfnSeg* b, hipStream_t st);
+// int8 codes [n_exp, rows, K] (gate/up pair when src1 != nullptr) -> code tiles
+hipError_t launch_w8_pack(const int8_t* src0, const int8_t* src1, int n_exp, int rows, int K,
+                          int8_t* dst, hipStream_t st);
+// bf16 weights [n_exp, rows, K] (gate/up pair when src1 != nullptr) -> code tiles
+// and per-row scales (scale0 for src0's rows, scale1 for src1's)
+hipError_t launch_w8_quantize(const void* src0, const void* src1, int n_exp, int rows, int K,
+                              int8_t* dst, float* scale0, float* scale1, hipStream_t st);
 
 // ---- expert FFN, MFMA tile path (tile_gemm.hip, bf16) ----------------------
 // Routed experts with at most kStreamMaxRows rows take the streaming kernels; those

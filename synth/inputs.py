@@ -14,7 +14,15 @@ Recipe (every tensor):
 
 Tensor ids: 0 x[T,d], 1 w_router[N,d], 2 w_gate[N,I,d], 3 w_up[N,I,d],
 4 w_down[N,d,I], 5 ws_gate[I_s,d], 6 ws_up[I_s,d], 7 ws_down[d,I_s],
-8 router scores for the routing-only calls [T,N] (std 1).
+8 router scores for the routing-only calls [T,N] (std 1),
+20-25 int8 expert codes (gate, up, down, shared gate, shared up, shared down),
+30-35 their per-row scales (same order).
+
+int8 expert weights (the weight-only int8 layer): codes are float32 draws of
+standard_normal * 32 with the chunked recipe above, rounded to the nearest integer
+and clipped to [-127, 127]; per-row scales are (w_std / 32) * (1 + 0.25 u), u
+uniform in [-1, 1) from SeedSequence([seed, tid]), so that scale * code has about
+the spread of the bf16 weights.
 
 Layouts are row-major with the contraction dimension contiguous for every weight:
 a gate/up row is one intermediate unit's d inputs, a down row is one output
@@ -36,6 +44,9 @@ from .configs import LayerConfig
 CHUNK = 1 << 20
 
 TID_X, TID_WR, TID_WG, TID_WU, TID_WD, TID_WSG, TID_WSU, TID_WSD, TID_SCORES = range(9)
+TID_QG, TID_QU, TID_QD, TID_QSG, TID_QSU, TID_QSD = range(20, 26)
+TID_SG, TID_SU, TID_SD, TID_SSG, TID_SSU, TID_SSD = range(30, 36)
+CODE_STD = 32.0
 
 
 def _threads() -> int:
@@ -123,6 +134,36 @@ def make_weights(cfg: LayerConfig, seed: Optional[int] = None) -> dict:
         ws_gate=normal_tensor((Is, d), cfg.w_std, seed, TID_WSG, dt),
         ws_up=normal_tensor((Is, d), cfg.w_std, seed, TID_WSU, dt),
         ws_down=normal_tensor((d, Is), cfg.w_std, seed, TID_WSD, dt),
+    )
+
+
+def int8_codes(shape, seed: int, tid: int) -> np.ndarray:
+    """Seeded int8 codes: rint(standard_normal * 32) clipped to [-127, 127]."""
+    v = normal_tensor(shape, CODE_STD, seed, tid, "f32")
+    return np.clip(np.rint(v), -127, 127).astype(np.int8)
+
+
+def row_scales(n: int, mean: float, seed: int, tid: int) -> np.ndarray:
+    """Seeded per-row scales mean * (1 + 0.25 u), u ~ U[-1, 1), float32."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid])))
+    u = g.random(n, dtype=np.float64) * 2.0 - 1.0
+    return (mean * (1.0 + 0.25 * u)).astype(np.float32)
+
+
+def make_w8_weights(cfg: LayerConfig, seed: Optional[int] = None) -> dict:
+    """int8 codes and float32 per-row scales of the expert and shared weights
+    (shapes of make_weights; scales [.., rows]).  The router keeps make_weights'
+    bf16 w_router."""
+    seed = cfg.seed if seed is None else seed
+    d, N, I, Is = cfg.d, cfg.N, cfg.inter, cfg.I_s
+    m = cfg.w_std / CODE_STD
+    return dict(
+        q_gate=int8_codes((N, I, d), seed, TID_QG), s_gate=row_scales(N * I, m, seed, TID_SG).reshape(N, I),
+        q_up=int8_codes((N, I, d), seed, TID_QU), s_up=row_scales(N * I, m, seed, TID_SU).reshape(N, I),
+        q_down=int8_codes((N, d, I), seed, TID_QD), s_down=row_scales(N * d, m, seed, TID_SD).reshape(N, d),
+        qs_gate=int8_codes((Is, d), seed, TID_QSG), ss_gate=row_scales(Is, m, seed, TID_SSG),
+        qs_up=int8_codes((Is, d), seed, TID_QSU), ss_up=row_scales(Is, m, seed, TID_SSU),
+        qs_down=int8_codes((d, Is), seed, TID_QSD), ss_down=row_scales(d, m, seed, TID_SSD),
     )
 
 

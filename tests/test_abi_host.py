@@ -127,3 +127,43 @@ def test_expert_ffn_and_combine_validation():
                                None) == 1
     assert lib.moge_combine(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, None) == 0
     assert lib.moge_combine(ctypes.byref(d), FAKE, FAKE, FAKE, MIS, FAKE, None) == 1
+
+
+def test_w8_entry_points_validation():
+    d = dims(T=0)
+    need = moge.workspace_size(d)
+    wsize = moge.w8_weights_size(d)
+    assert wsize > 0 and wsize % 256 == 0
+    P = FAKE
+
+    def fwd(dd, **over):
+        a = dict(x=P, w_router=P, bias=None, w8=P, lin=None, y=P, ws=P, wsb=need)
+        a.update(over)
+        return lib.moge_layer_forward_w8(ctypes.byref(dd), a["x"], a["w_router"], a["bias"],
+                                         a["w8"], a["lin"], a["y"], None, None, None, None,
+                                         a["ws"], a["wsb"], None)
+    assert fwd(d) == 0
+    assert fwd(d, w8=None) == 1 and "w8 is NULL" in moge.last_error()
+    assert fwd(d, w8=FAKE + 16) == 1 and "256-byte" in moge.last_error()
+    assert fwd(d, wsb=0) == 3
+    assert fwd(dims(T=0, dtype=moge.MOGE_F32)) == 2 and "bf16" in moge.last_error()
+    assert fwd(dims(T=0, inter=1312)) == 2 and "multiples of 64" in moge.last_error()
+    assert fwd(dims(T=0, d=5088)) == 2 and "multiples of 64" in moge.last_error()
+
+    # pack: codes must be 16-byte aligned, the buffer large enough (no call here
+    # passes validation: these entry points launch kernels whatever T is)
+    codes = [P] * 3 + [P] * 3 + [P] * 3 + [P] * 3
+    st = lib.moge_pack_weights_w8(ctypes.byref(d), MIS, *codes[1:], P, wsize, None)
+    assert st == 1 and "q_gate" in moge.last_error()
+    st = lib.moge_pack_weights_w8(ctypes.byref(d), *codes, P, wsize - 1, None)
+    assert st == 1 and "need" in moge.last_error()
+    st = lib.moge_pack_weights_w8(ctypes.byref(d), *codes[:6], None, *codes[7:], P, wsize, None)
+    assert st == 1 and "qs_gate" in moge.last_error()
+    # quantise
+    st = lib.moge_quantize_weights_w8(ctypes.byref(d), P, P, MIS, P, P, P, P, wsize, None)
+    assert st == 1 and "w_down" in moge.last_error()
+    st = lib.moge_quantize_weights_w8(ctypes.byref(d), P, P, P, P, P, P, P, 0, None)
+    assert st == 1 and "need" in moge.last_error()
+    st = lib.moge_quantize_weights_w8(ctypes.byref(dims(T=0, dtype=moge.MOGE_F32)), P, P, P, P,
+                                      P, P, P, wsize, None)
+    assert st == 2

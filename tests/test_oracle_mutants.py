@@ -133,3 +133,45 @@ def test_mutant_group_count_off_by_one(monkeypatch):
         return r
     monkeypatch.setattr(O, "permute", mutant)
     _fails(P.test_group_loads_equal_imbalance_zero)
+
+
+def test_mutant_w8_truncating_codes(monkeypatch):
+    def mutant(w, dtype):
+        w32 = O.to_f64(w, dtype).astype(np.float32)
+        s = (np.max(np.abs(w32), axis=-1) / np.float32(127)).astype(np.float32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = np.trunc(w32 / s[..., None])
+        return np.where(s[..., None] > 0, np.clip(r, -127, 127), 0).astype(np.int8), s
+    monkeypatch.setattr(O, "w8_quantize", mutant)
+    _fails(P.test_w8_quantize_golden_rows)
+    _fails(P.test_w8_quantize_error_bound_and_range, "f32")
+
+
+def test_mutant_w8_scale_over_128(monkeypatch):
+    real = O.w8_quantize
+
+    def mutant(w, dtype):
+        q, s = real(w, dtype)
+        w32 = O.to_f64(w, dtype).astype(np.float32)
+        s = (np.max(np.abs(w32), axis=-1) / np.float32(128)).astype(np.float32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = np.rint(w32 / s[..., None])
+        return np.where(s[..., None] > 0, np.clip(r, -127, 127), 0).astype(np.int8), s
+    monkeypatch.setattr(O, "w8_quantize", mutant)
+    _fails(P.test_w8_quantize_error_bound_and_range, "f32")
+
+
+def test_mutant_w8_scale_along_contraction(monkeypatch):
+    class Mutant(O.W8Weights):
+        def __getitem__(self, e):
+            q = self.q[e].astype(np.float64)
+            s = self.s[e].astype(np.float64)
+            k = q.shape[-1]
+            # scales applied along the contraction index instead of the output row
+            return q * np.resize(s, k)[None, :]
+
+        def __array__(self, dtype=None, copy=None):
+            return np.stack([self[i] for i in range(self.q.shape[0])]) if self.q.ndim == 3 \
+                else self.q.astype(np.float64) * np.resize(self.s, self.q.shape[-1])[None, :]
+    monkeypatch.setattr(O, "W8Weights", Mutant)
+    _fails(P.test_w8_layer_is_the_layer_on_exactly_quantisable_weights)

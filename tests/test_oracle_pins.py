@@ -379,3 +379,73 @@ def test_c0_layer_runs_fast_and_is_balanced():
     assert out["y"].shape == (C0.T, C0.d)
     assert (out["group_counts"] == C0.T).all()
     assert np.isfinite(out["y"]).all()
+
+
+# ----------------------------------------------------------------------------
+# int8 expert weights (reading Q1)
+# ----------------------------------------------------------------------------
+
+def test_w8_quantize_golden_rows():
+    with open(os.path.join(GOLDEN, "w8_quantize_small.json")) as f:
+        g = json.load(f)
+    q, s = O.w8_quantize(np.array(g["rows"], dtype=np.float32), "f32")
+    np.testing.assert_array_equal(s, np.array(g["scales"], dtype=np.float32))
+    np.testing.assert_array_equal(q, np.array(g["codes"], dtype=np.int8))
+    assert q.dtype == np.int8 and s.dtype == np.float32
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_w8_quantize_error_bound_and_range(dtype):
+    # every code is within half a step of the weight it stands for, the largest
+    # weight of a row maps to +-127, and no code leaves [-127, 127]
+    rng = _rng(31)
+    w = (rng.standard_t(3, size=(40, 3, 96)) * 0.02).astype(np.float32)
+    w[3, 1] = 0.0
+    wb = S.f32_to_bf16_bits(w) if dtype == "bf16" else w
+    q, s = O.w8_quantize(wb, dtype)
+    w64 = S.bf16_bits_to_f32(wb).astype(np.float64) if dtype == "bf16" else w.astype(np.float64)
+    s64 = s.astype(np.float64)[..., None]
+    assert q.shape == w.shape and s.shape == w.shape[:-1]
+    assert np.abs(q.astype(np.int64)).max() <= 127
+    assert (np.abs(q.astype(np.float64) * s64 - w64) <= s64 * (0.5 + 1e-5)).all()
+    nz = np.abs(w64).max(-1) > 0
+    assert (np.abs(q.astype(np.int64)).max(-1)[nz] == 127).all()
+    assert (s[~nz] == 0).all() and (q[~nz] == 0).all()
+
+
+def _exact_w8_weights(rng, *shape):
+    """float32 weights whose rows are integers (largest magnitude 127) times a
+    power of two, with the codes and scales they quantise to by construction."""
+    ints = rng.integers(-127, 128, size=shape)
+    flat = ints.reshape(-1, shape[-1])
+    for r in range(flat.shape[0]):
+        flat[r, rng.integers(shape[-1])] = 127 if rng.random() < 0.5 else -127
+    ints = flat.reshape(shape)
+    e = rng.integers(6, 10, size=shape[:-1]).astype(np.float64)
+    scale = np.exp2(-e)
+    w = (ints * scale[..., None]).astype(np.float32)
+    return w, ints.astype(np.int8), scale.astype(np.float32)
+
+
+def test_w8_layer_is_the_layer_on_exactly_quantisable_weights():
+    # weights that are exactly integers times a per-row power of two quantise to
+    # those integers and scales, and the int8 layer on them is the float layer
+    rng = _rng(33)
+    N, M, d, I, Is, T = 6, 2, 8, 4, 6, 9
+    wg, qg, sg = _exact_w8_weights(rng, N, I, d)
+    wu, qu, su = _exact_w8_weights(rng, N, I, d)
+    wd, qd, sd = _exact_w8_weights(rng, N, d, I)
+    wsg, qsg, ssg = _exact_w8_weights(rng, Is, d)
+    wsu, qsu, ssu = _exact_w8_weights(rng, Is, d)
+    wsd, qsd, ssd = _exact_w8_weights(rng, d, Is)
+    for w, q, s in ((wg, qg, sg), (wd, qd, sd), (wsd, qsd, ssd)):
+        q2, s2 = O.w8_quantize(w, "f32")
+        np.testing.assert_array_equal(q2, q)
+        np.testing.assert_array_equal(s2, s)
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    wr = rng.normal(size=(N, d)).astype(np.float32)
+    ref = O.layer(x, wr, None, wg, wu, wd, wsg, wsu, wsd, M=M, kp=1, dtype="f32")
+    got = O.layer_w8(x, wr, None, qg, sg, qu, su, qd, sd, qsg, ssg, qsu, ssu, qsd, ssd, M=M,
+                     kp=1, dtype="f32")
+    np.testing.assert_array_equal(got["idx"], ref["idx"])
+    np.testing.assert_array_equal(got["y"], ref["y"])

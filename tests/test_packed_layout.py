@@ -96,3 +96,57 @@ def test_packed_layer_equals_row_major_layer(lib, name, T, given):
                               logits_in=logits_in)
     torch.cuda.synchronize()
     assert np.array_equal(to_host(ya), to_host(yb))
+
+
+# ----------------------------------------------------------------------------
+# int8 expert weights
+# ----------------------------------------------------------------------------
+
+def test_w8_layout_first_tiles_and_size():
+    rng = np.random.Generator(np.random.PCG64(5))
+    N, I, d, Is = 2, 64, 128, 64
+    q = lambda *s: rng.integers(-127, 128, size=s).astype(np.int8)
+    f = lambda *s: rng.random(s).astype(np.float32)
+    qg, qu, qd, qsg, qsu, qsd = q(N, I, d), q(N, I, d), q(N, d, I), q(Is, d), q(Is, d), q(d, Is)
+    sg, su, sd, ssg, ssu, ssd = f(N, I), f(N, I), f(N, d), f(Is), f(Is), f(d)
+    buf = packed_ref.w8_buffer(qg, sg, qu, su, qd, sd, qsg, ssg, qsu, ssu, qsd, ssd)
+    dims = moge.make_dims(1, d, N, 1, 1, I, Is, moge.MOGE_BF16)
+    assert moge.w8_weights_size(dims) == buf.size
+    codes = buf.view(np.int8)
+    # first tile: gate rows 0..15 of expert 0, elements 0..63; chunk l = row l%16,
+    # elements 16*(l//16) .. +15
+    t0 = codes[:1024].reshape(64, 16)
+    t1 = codes[1024:2048].reshape(64, 16)
+    for l in range(64):
+        assert list(t0[l]) == list(qg[0, l % 16, 16 * (l // 16): 16 * (l // 16) + 16])
+        assert list(t1[l]) == list(qu[0, l % 16, 16 * (l // 16): 16 * (l // 16) + 16])
+    # second step of block 0 follows: elements 64..127
+    t2 = codes[2048:3072].reshape(64, 16)
+    assert list(t2[5]) == list(qg[0, 5, 64:80])
+    # down part of expert 0: tiles of rows 0..15 and 16..31, step 0
+    off, _ = packed_ref.w8_regions(d, N, I, Is)
+    o = off["routed_down"][0]
+    d0 = codes[o:o + 1024].reshape(64, 16)
+    d1 = codes[o + 1024:o + 2048].reshape(64, 16)
+    for l in range(64):
+        assert list(d0[l]) == list(qd[0, l % 16, 16 * (l // 16): 16 * (l // 16) + 16])
+        assert list(d1[l]) == list(qd[0, 16 + l % 16, 16 * (l // 16): 16 * (l // 16) + 16])
+    # scales sit where the regions say, as float32
+    o = off["s_down"][0]
+    np.testing.assert_array_equal(buf[o:o + 4 * N * d].view(np.float32).reshape(N, d), sd)
+    # the unpacking inverts the packing
+    u = packed_ref.w8_unpack(buf, d, N, I, Is)
+    for e in range(N):
+        np.testing.assert_array_equal(u["q_gate"][e], qg[e])
+        np.testing.assert_array_equal(u["q_up"][e], qu[e])
+        np.testing.assert_array_equal(u["q_down"][e], qd[e])
+    np.testing.assert_array_equal(u["qs_gate"], qsg)
+    np.testing.assert_array_equal(u["qs_down"], qsd)
+    np.testing.assert_array_equal(u["ss_up"], ssu)
+
+
+def test_w8_size_rejects_unsupported_dims():
+    assert moge.w8_weights_size(moge.make_dims(1, 96, 4, 1, 1, 64, 0, moge.MOGE_BF16)) == 0
+    assert moge.w8_weights_size(moge.make_dims(1, 128, 4, 1, 1, 96, 0, moge.MOGE_BF16)) == 0
+    assert moge.w8_weights_size(moge.make_dims(1, 128, 4, 1, 1, 64, 0, moge.MOGE_F32)) == 0
+    assert moge.w8_weights_size(moge.make_dims(1, 128, 4, 1, 1, 64, 0, moge.MOGE_BF16)) > 0
