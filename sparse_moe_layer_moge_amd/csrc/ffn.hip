@@ -26,11 +26,17 @@ namespace moge {
 // not depend on how blocks are grouped into waves.
 constexpr int kStartStep = 0;
 
+// Narrow segments get an even number of blocks per wave, so that the paired
+// (two blocks per step) stream applies.
+constexpr int kPairBlocks = 2;
+
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU: H[r, f] = silu(x_r . Wg[f]) * (x_r . Wu[f]) for the features
 // f of `nblk` consecutive 16-feature blocks starting at block b0
 // ---------------------------------------------------------------------------
-template <typename E, int MS, int PW>
+// BPS blocks per step: with BPS = 2 the wave streams two blocks side by side, so
+// each activation fragment serves four weight tiles.
+template <typename E, int MS, int PW, int BPS>
 __device__ __forceinline__ void gateup_pass(const FfnSeg& g, int d, int e, int b0, int nblk,
                                             int lo, int cnt, int m0, int s0) {
   const int l = threadIdx.x & 63, ln = l & 15, kq = (l >> 4) * 8;
@@ -43,14 +49,24 @@ __device__ __forceinline__ void gateup_pass(const FfnSeg& g, int d, int e, int b
   const uint32_t tb = kTileElems * sizeof(E);
   const uint32_t po = (uint32_t)(b0 * nsteps * 2) * tb + l * 8 * sizeof(E);
   const uint32_t wo = (uint32_t)(((b0 * 16 + ln) * d + kq) * sizeof(E));
-  const Rsrc wr[2] = {
-      packed ? make_rsrc(pbase, 2 * expert_elems * sizeof(E))
-             : make_rsrc(static_cast<const E*>(g.w_gate) + e * expert_elems, expert_elems * sizeof(E)),
-      packed ? make_rsrc(pbase, 2 * expert_elems * sizeof(E))
-             : make_rsrc(static_cast<const E*>(g.w_up) + e * expert_elems, expert_elems * sizeof(E))};
-  const uint32_t wv[2] = {packed ? po : wo, packed ? po + tb : wo};
+  const Rsrc rg = packed ? make_rsrc(pbase, 2 * expert_elems * sizeof(E))
+                         : make_rsrc(static_cast<const E*>(g.w_gate) + e * expert_elems,
+                                     expert_elems * sizeof(E));
+  const Rsrc ru = packed ? make_rsrc(pbase, 2 * expert_elems * sizeof(E))
+                         : make_rsrc(static_cast<const E*>(g.w_up) + e * expert_elems,
+                                     expert_elems * sizeof(E));
   const uint32_t wstep = packed ? 2 * tb : 32 * sizeof(E);
   const uint32_t blk_bytes = packed ? nsteps * 2 * tb : 16 * d * sizeof(E);
+  // tile 2*sb + t: gate (t = 0) or up (t = 1) rows of block sb of the group
+  Rsrc wr[2 * BPS];
+  uint32_t wv[2 * BPS];
+#pragma unroll
+  for (int sb = 0; sb < BPS; ++sb) {
+    wr[2 * sb] = rg;
+    wr[2 * sb + 1] = ru;
+    wv[2 * sb] = (packed ? po : wo) + sb * blk_bytes;
+    wv[2 * sb + 1] = (packed ? po + tb : wo) + sb * blk_bytes;
+  }
   const Rsrc xr = make_rsrc(g.x, (uint64_t)g.x_rows * d * sizeof(E));
   uint32_t xv[MS];
 #pragma unroll
@@ -62,16 +78,20 @@ __device__ __forceinline__ void gateup_pass(const FfnSeg& g, int d, int e, int b
   E* const h = static_cast<E*>(g.h);
   const int I = g.inter;
   // lane l holds features 16*b + 4*(l/16) + i of row m0 + ms*16 + l%16
-  stream_blocks<E, 2, MS, PW>(wr, wv, wstep, blk_bytes, xr, xv, nsteps, nblk, s0,
-                              [&](int blk, const f32x4 (&acc)[2][MS]) {
+  stream_blocks<E, 2 * BPS, MS, PW>(wr, wv, wstep, BPS * blk_bytes, xr, xv, nsteps, nblk / BPS,
+                                     s0, [&](int grp, const f32x4 (&acc)[2 * BPS][MS]) {
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      const int rr = m0 + ms * 16 + ln;
-      if (rr < cnt) {
-        f32x4 hv;
+    for (int sb = 0; sb < BPS; ++sb) {
+      const int blk = grp * BPS + sb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hv[i] = silu(acc[0][ms][i]) * acc[1][ms][i];
-        store4(h + (size_t)(lo + rr) * I + (b0 + blk) * 16 + 4 * (l >> 4), hv);
+      for (int ms = 0; ms < MS; ++ms) {
+        const int rr = m0 + ms * 16 + ln;
+        if (rr < cnt) {
+          f32x4 hv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[i] = silu(acc[2 * sb][ms][i]) * acc[2 * sb + 1][ms][i];
+          store4(h + (size_t)(lo + rr) * I + (b0 + blk) * 16 + 4 * (l >> 4), hv);
+        }
       }
     }
   });
@@ -81,10 +101,14 @@ template <typename E, int MS>
 __device__ __forceinline__ void gateup_dispatch_depth(const FfnSeg& g, int d, int e, int b0,
                                                       const SegView& v, int m0, int s0) {
   constexpr int PW = StreamDepth<E, MS>::value;
-  if ((d / 32) * g.nblk >= PW)
-    gateup_pass<E, MS, PW>(g, d, e, b0, g.nblk, v.lo, v.cnt, m0, s0);
+  constexpr int PW2 = StreamPair<E, MS>::depth;
+  const int nsteps = d / 32;
+  if (PW2 > 0 && g.nblk % 2 == 0 && nsteps * (g.nblk / 2) >= PW2)
+    gateup_pass<E, MS, (PW2 > 0 ? PW2 : 1), 2>(g, d, e, b0, g.nblk, v.lo, v.cnt, m0, s0);
+  else if (nsteps * g.nblk >= PW)
+    gateup_pass<E, MS, PW, 1>(g, d, e, b0, g.nblk, v.lo, v.cnt, m0, s0);
   else
-    gateup_pass<E, MS, 1>(g, d, e, b0, g.nblk, v.lo, v.cnt, m0, s0);
+    gateup_pass<E, MS, 1, 1>(g, d, e, b0, g.nblk, v.lo, v.cnt, m0, s0);
 }
 
 template <typename E>
@@ -115,7 +139,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_
 // down projection: y[r, 32b .. 32b+31] = H[r,:] . W_down[e, 32b .. 32b+31, :]
 // for `nblk` consecutive 32-row blocks starting at block b0
 // ---------------------------------------------------------------------------
-template <typename E, int MS, int PW>
+template <typename E, int MS, int PW, int BPS>
 __device__ __forceinline__ void down_pass(const FfnSeg& g, int d, int e, int b0, int nblk, int lo,
                                           int cnt, int m0, int s0) {
   const int l = threadIdx.x & 63, ln = l & 15, kq = (l >> 4) * 8;
@@ -128,29 +152,40 @@ __device__ __forceinline__ void down_pass(const FfnSeg& g, int d, int e, int b0,
                                     expert_elems * sizeof(E))
                         : make_rsrc(static_cast<const E*>(g.w_down) + e * expert_elems,
                                     expert_elems * sizeof(E));
-  const Rsrc wr[2] = {w, w};
   // packed: rows 32b..32b+15 and 32b+16..32b+31 of a step are adjacent tiles
   const uint32_t po = (uint32_t)(b0 * nsteps * 2) * tb + l * 8 * sizeof(E);
   const uint32_t wo = (uint32_t)(((b0 * 32 + ln) * I + kq) * sizeof(E));
-  const uint32_t wv[2] = {packed ? po : wo,
-                          packed ? po + tb : wo + (uint32_t)(16 * I * sizeof(E))};
   const uint32_t wstep = packed ? 2 * tb : 32 * sizeof(E);
   const uint32_t blk_bytes = packed ? nsteps * 2 * tb : 32 * I * sizeof(E);
+  // tile 2*sb + t: rows 32*(b0+blk) + 16t .. +15 of block sb of the group
+  Rsrc wr[2 * BPS];
+  uint32_t wv[2 * BPS];
+#pragma unroll
+  for (int sb = 0; sb < BPS; ++sb) {
+    wr[2 * sb] = w;
+    wr[2 * sb + 1] = w;
+    wv[2 * sb] = (packed ? po : wo) + sb * blk_bytes;
+    wv[2 * sb + 1] = (packed ? po + tb : wo + (uint32_t)(16 * I * sizeof(E))) + sb * blk_bytes;
+  }
   const Rsrc xr = make_rsrc(g.h, (uint64_t)g.rows * I * sizeof(E));
   uint32_t xv[MS];
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms)
     xv[ms] = (uint32_t)(((size_t)(lo + min(m0 + ms * 16 + ln, cnt - 1)) * I + kq) * sizeof(E));
   E* const y = static_cast<E*>(g.y);
-  stream_blocks<E, 2, MS, PW>(wr, wv, wstep, blk_bytes, xr, xv, nsteps, nblk, s0,
-                              [&](int blk, const f32x4 (&acc)[2][MS]) {
+  stream_blocks<E, 2 * BPS, MS, PW>(wr, wv, wstep, BPS * blk_bytes, xr, xv, nsteps, nblk / BPS,
+                                     s0, [&](int grp, const f32x4 (&acc)[2 * BPS][MS]) {
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      const int rr = m0 + ms * 16 + ln;
-      if (rr < cnt) {
-        E* out = y + (size_t)(lo + rr) * d + (b0 + blk) * 32 + 4 * (l >> 4);
-        store4(out, acc[0][ms]);
-        store4(out + 16, acc[1][ms]);
+    for (int sb = 0; sb < BPS; ++sb) {
+      const int blk = grp * BPS + sb;
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        const int rr = m0 + ms * 16 + ln;
+        if (rr < cnt) {
+          E* out = y + (size_t)(lo + rr) * d + (b0 + blk) * 32 + 4 * (l >> 4);
+          store4(out, acc[2 * sb][ms]);
+          store4(out + 16, acc[2 * sb + 1][ms]);
+        }
       }
     }
   });
@@ -160,10 +195,14 @@ template <typename E, int MS>
 __device__ __forceinline__ void down_dispatch_depth(const FfnSeg& g, int d, int e, int b0,
                                                     const SegView& v, int m0, int s0) {
   constexpr int PW = StreamDepth<E, MS>::value;
-  if ((g.inter / 32) * g.nblk >= PW)
-    down_pass<E, MS, PW>(g, d, e, b0, g.nblk, v.lo, v.cnt, m0, s0);
+  constexpr int PW2 = StreamPair<E, MS>::depth;
+  const int nsteps = g.inter / 32;
+  if (PW2 > 0 && g.nblk % 2 == 0 && nsteps * (g.nblk / 2) >= PW2)
+    down_pass<E, MS, (PW2 > 0 ? PW2 : 1), 2>(g, d, e, b0, g.nblk, v.lo, v.cnt, m0, s0);
+  else if (nsteps * g.nblk >= PW)
+    down_pass<E, MS, PW, 1>(g, d, e, b0, g.nblk, v.lo, v.cnt, m0, s0);
   else
-    down_pass<E, MS, 1>(g, d, e, b0, g.nblk, v.lo, v.cnt, m0, s0);
+    down_pass<E, MS, 1, 1>(g, d, e, b0, g.nblk, v.lo, v.cnt, m0, s0);
 }
 
 template <typename E>
@@ -249,7 +288,7 @@ hipError_t launch_ffn_gateup(int dtype, int d, const FfnSeg& a0, const FfnSeg* b
   FfnSeg a = a0, bb = b0 ? *b0 : FfnSeg{};
   // a block = 16 gate rows + 16 up rows over the whole contraction
   plan_blocks(a, b0 ? &bb : nullptr, 32.0 * d * es, 32.0 * d * es, a.inter / 16,
-              b0 ? bb.inter / 16 : 0);
+              b0 ? bb.inter / 16 : 0, kPairBlocks);
   const int items_a = a.n_exp * (a.inter / 16 / a.nblk);
   const int items_b = b0 ? bb.n_exp * (bb.inter / 16 / bb.nblk) : 0;
   if (items_a + items_b == 0) return hipSuccess;
@@ -266,7 +305,7 @@ hipError_t launch_ffn_down(int dtype, int d, const FfnSeg& a0, const FfnSeg* b0,
   FfnSeg a = a0, bb = b0 ? *b0 : FfnSeg{};
   // a block = 32 down rows over the segment's intermediate width
   plan_blocks(a, b0 ? &bb : nullptr, 32.0 * a.inter * es, b0 ? 32.0 * bb.inter * es : 0.0,
-              d / 32, b0 ? d / 32 : 0);
+              d / 32, b0 ? d / 32 : 0, kPairBlocks);
   const int items_a = a.n_exp * (d / 32 / a.nblk);
   const int items_b = b0 ? bb.n_exp * (d / 32 / bb.nblk) : 0;
   if (items_a + items_b == 0) return hipSuccess;

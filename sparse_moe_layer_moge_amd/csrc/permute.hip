@@ -18,10 +18,9 @@
 
 namespace moge {
 
-constexpr int kSmallWaves = 16;    // waves of the single-workgroup kernel
-constexpr int kSmallChunks = 64;   // chunks it can hold (T <= 4096)
-constexpr int kSmallUseChunks = 8; // chunks up to which it is used: beyond that the
-                                   // chunk-parallel kernels finish sooner
+constexpr int kSmallWaves = 16;  // waves of the single-workgroup kernel
+constexpr int kSmallChunks = 8;  // chunks up to which it is used (T <= 512): beyond
+                                 // that the chunk-parallel kernels finish sooner
 
 // f(k, e) for every slot k of token t, in slot order.  The slot indices are
 // loaded 8 at a time before any is used, so a token's loads overlap instead of
@@ -134,55 +133,86 @@ __device__ __forceinline__ void expert_offsets(const int32_t* cnt, int N, int32_
 }
 
 // ---------------------------------------------------------------------------
-// single workgroup: T <= 64 * kSmallChunks
+// single workgroup: T <= 64 * kSmallChunks.  The masks and counts are split by
+// (chunk, slice of the experts) and the scatter by (chunk, slot), so that a
+// decode batch of one chunk still spreads over every wave.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64 * kSmallWaves) void k_permute_small(
     const int32_t* __restrict__ idx, int T, int K, int N, int M, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ group_counts,
     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row) {
-  __shared__ int32_t s_base[kSmallChunks][256];     // counts, then prefix over chunks
-  __shared__ uint64_t s_mask[kSmallWaves][256];
+  __shared__ uint64_t s_mask[kSmallChunks][256];  // tokens of chunk c that chose e
+  __shared__ int32_t s_base[kSmallChunks][256];   // those tokens in chunks before c
   __shared__ int32_t s_cnt[256];
   __shared__ int32_t s_off[257];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int nchunks = (T + 63) / 64;
 
-  // per chunk and expert: tokens of the chunk that chose the expert
-  for (int c = w; c < nchunks; c += kSmallWaves) {
+  // masks and per-chunk counts: wave w takes chunk w % nchunks and every S-th
+  // expert from w / nchunks on (S waves per chunk)
+  const int S = nchunks > 0 ? max(1, kSmallWaves / nchunks) : 1;
+  if (w < nchunks * S) {
+    const int c = w % nchunks, sl = w / nchunks;
     uint64_t chosen[4];
     chosen_set(idx, c * 64 + l, K, N, c * 64 + l < T, chosen);
-    chunk_counts(chosen, N, s_base[c]);
-  }
-  __syncthreads();
-  // per expert: exclusive prefix over the chunks (lane = chunk), total = count
-  for (int e = w; e < N; e += kSmallWaves) {
-    const int v = l < nchunks ? s_base[l][e] : 0;
-    const int incl = wave_incl_scan(v);
-    if (l < nchunks) s_base[l][e] = incl - v;
-    if (l == 63) {
-      s_cnt[e] = incl;
-      counts[e] = incl;
+    for (int e = sl; e < N; e += S) {
+      const uint64_t m = __ballot(in_set(chosen, e));
+      if (l == 0) {
+        s_mask[c][e] = m;
+        if (nchunks == 1) {  // one chunk: its count is the total, nothing before it
+          s_base[0][e] = 0;
+          s_cnt[e] = __popcll(m);
+          counts[e] = __popcll(m);
+        } else {
+          s_base[c][e] = __popcll(m);
+        }
+      }
     }
   }
   __syncthreads();
+  if (nchunks > 1) {
+    // per expert: exclusive prefix over the chunks (lane = chunk), total = count
+    for (int e = w; e < N; e += kSmallWaves) {
+      const int v = l < nchunks ? s_base[l][e] : 0;
+      const int incl = wave_incl_scan(v);
+      if (l < nchunks) s_base[l][e] = incl - v;
+      if (l == 63) {
+        s_cnt[e] = incl;
+        counts[e] = incl;
+      }
+    }
+    __syncthreads();
+  }
   if (w == 0) expert_offsets(s_cnt, N, s_off);
   __syncthreads();
   for (int e = threadIdx.x; e <= N; e += blockDim.x) offsets[e] = s_off[e];
   const int G = N / M;
   for (int g = threadIdx.x; g < M; g += blockDim.x) group_counts[g] = s_off[(g + 1) * G] - s_off[g * G];
-  for (int c = w; c < nchunks; c += kSmallWaves) {
-    const int t = c * 64 + l;
-    uint64_t chosen[4];
-    chosen_set(idx, t, K, N, t < T, chosen);
-    chunk_masks(chosen, N, s_mask[w]);
-    // lane 0's mask stores must be visible to the whole wave before the reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    chunk_scatter(idx, t, K, N, t < T, s_off, s_base[c], s_mask[w], sorted_pair, pair_row);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // scatter: unit (chunk c, slot k); lane = token.  row = offset of the expert +
+  // its tokens in earlier chunks + its tokens earlier in this chunk.  A slot whose
+  // expert is out of range or repeats an earlier slot of the token gets no row.
+  const uint64_t lt = lanemask_lt();
+  for (int u = w; u < nchunks * K; u += kSmallWaves) {
+    const int c = u / K, k = u - c * K, t = c * 64 + l;
+    if (t >= T) continue;
+    const int32_t* p = idx + (size_t)t * K;
+    const int e = p[k];
+    bool keep = (unsigned)e < (unsigned)N;
+    // the earlier slots, loaded 8 at a time before any is compared
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = j0 + j < k ? p[j0 + j] : -1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) keep = keep && v[j] != e;
+    }
+    int row = -1;
+    if (keep) {
+      row = s_off[e] + s_base[c][e] + __popcll(s_mask[c][e] & lt);
+      sorted_pair[row] = t * K + k;
+    }
+    pair_row[(size_t)t * K + k] = row;
   }
 }
 
@@ -254,7 +284,7 @@ hipError_t launch_permute(const int32_t* idx, int T, int K, int N, int M, int32_
                           int32_t* group_counts, int32_t* sorted_pair, int32_t* pair_row,
                           hipStream_t st) {
   const int nblk = perm_blocks(T);
-  if (nblk <= kSmallUseChunks) {
+  if (nblk <= kSmallChunks) {
     hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(64 * kSmallWaves), 0, st, idx, T, K, N, M,
                        counts, offsets, group_counts, sorted_pair, pair_row);
     return hipGetLastError();

@@ -154,4 +154,9 @@ template <> struct StreamDepth<float, 2> { static constexpr int value = 2; };
 template <> struct StreamDepth<float, 3> { static constexpr int value = 2; };
 template <> struct StreamDepth<float, 4> { static constexpr int value = 1; };
 
+// Depth of the paired stream (two row blocks per step sharing the activation
+// fragments); 0 = no paired variant for this subtile count.
+template <typename E, int MS> struct StreamPair { static constexpr int depth = 0; };
+template <> struct StreamPair<bf16, 1> { static constexpr int depth = 5; };
+
 }  // namespace moge

@@ -119,6 +119,32 @@ def test_permute_bit_exact(lib, name, T):
     assert torch.equal(x_perm, x.index_select(0, src))
 
 
+@pytest.mark.parametrize("T", [64, 300, 512, 513, 2000])
+def test_permute_arbitrary_choices(lib, T):
+    # K distinct experts per token, not one per group and heavily skewed (expert 0
+    # in most tokens): uneven counts and group loads; 512/513 straddle the switch
+    # from the single-workgroup kernel to the chunk-parallel ones
+    import torch
+    cfg = C1
+    rng = np.random.Generator(np.random.PCG64(T))
+    w = 1.0 / np.arange(1, cfg.N + 1) ** 1.5
+    idx = np.stack([rng.choice(cfg.N, size=cfg.K, replace=False, p=w / w.sum())
+                    for _ in range(T)]).astype(np.int32)
+    ref = O.permute(idx, cfg.N, cfg.M)
+    dims = dims_of(lib, cfg, T)
+    out = {k: _empty(n, torch.int32) for k, n in
+           (("counts", cfg.N), ("offsets", cfg.N + 1), ("group_counts", cfg.M),
+            ("sorted_pair", dims.R), ("pair_row", dims.R))}
+    ws = _empty(lib.workspace_size(dims), torch.uint8)
+    say("permute arbitrary", T)
+    lib.permute(dims, to_dev(idx, "f32"), None, out["counts"], out["offsets"],
+                out["group_counts"], out["sorted_pair"], out["pair_row"], None, ws)
+    torch.cuda.synchronize()
+    for k in out:
+        np.testing.assert_array_equal(to_host(out[k]), ref[k], err_msg=k)
+    assert ref["counts"][0] > T // 2
+
+
 # ----------------------------------------------------------------------------
 # expert FFN (step API) and shared experts through the same entry point
 # ----------------------------------------------------------------------------
