@@ -92,9 +92,12 @@ hipError_t launch_w8_quantize(const void* src0, const void* src1, int n_exp, int
 // or kSharedSmallDownRows (down): a single segment of a few hundred rows has too
 // few 256-row tiles to fill the CUs (the down projection, with 256 output columns
 // per tile, far fewer than gate/up), while in the launch of the routed experts it
-// shares them.  The limits are measured choices on MI355X.
+// shares them.  A streamed segment of more than 32 rows keeps three or four row
+// subtiles of activations in registers and so few weight steps in flight; the
+// 64-row tiles stage both operands in LDS instead.  The limits are measured
+// choices on MI355X.
 constexpr int kStreamMaxRows = 32;
-constexpr int kSharedStreamMaxRows = 64;
+constexpr int kSharedStreamMaxRows = 32;
 constexpr int kSmallTileMaxRows = 128;
 constexpr int kSharedSmallGateUpRows = 128;
 constexpr int kSharedSmallDownRows = 512;
