@@ -121,9 +121,31 @@ moge_status_t check_w8_dims(const moge_dims_t* d) {
 // ---------------------------------------------------------------------------
 struct Plan {
   size_t partial, idx, gate, blk_cnt, blk_base, counts, offsets, gcounts, sorted_pair, pair_row,
-      h, hs, y_perm, sh, total;
+      h, hs, y_perm, sh, sh_part, total;
   int ksplit;
 };
+
+// Contraction slices of the shared experts' 64-row tile launches (gate/up, down);
+// 1 = not split.  A single segment of a few dozen rows makes too few tiles to
+// cover the CUs, so its contraction is split and the float32 partial sums are
+// added afterwards (gate/up: by k_swiglu_parts, down: by the combine).
+struct SharedSplit {
+  int gu = 1, dn = 1;
+};
+
+bool tiles_ok_for(const moge_dims_t* d) {
+  return d->dtype == MOGE_BF16 && moge::tile_path_ok(d->d, d->inter) &&
+         (d->shared_inter == 0 || moge::tile_path_ok(d->d, d->shared_inter));
+}
+
+SharedSplit shared_split(const moge_dims_t* d) {
+  SharedSplit s;
+  const int T = d->T, Is = d->shared_inter;
+  if (Is == 0 || !tiles_ok_for(d) || T <= moge::kSharedStreamMaxRows) return s;
+  if (T <= moge::kSharedSmallGateUpRows) s.gu = moge::tile_ksplit(T, d->d, Is / 64);
+  if (T <= moge::kSharedSmallDownRows) s.dn = moge::tile_ksplit(T, Is, d->d / 128);
+  return s;
+}
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -152,6 +174,11 @@ Plan make_plan(const moge_dims_t* d) {
   p.hs = take(T * (size_t)d->shared_inter * es);
   p.y_perm = take(R * (size_t)d->d * es);
   p.sh = take(T * (size_t)d->d * es);
+  const SharedSplit ss = shared_split(d);
+  size_t part = 0;
+  if (ss.gu > 1) part = (size_t)2 * ss.gu * T * d->shared_inter * 4;
+  if (ss.dn > 1 && (size_t)ss.dn * T * d->d * 4 > part) part = (size_t)ss.dn * T * d->d * 4;
+  p.sh_part = take(part);
   p.total = o;
   return p;
 }
@@ -205,8 +232,11 @@ moge::TileSeg tile_view(const moge::FfnSeg& f, bool gateup) {
 // its own limits (kSharedStreamMaxRows, kSharedSmallGateUpRows, kSharedSmallDownRows).  A tile launch is
 // made only when some expert can fall in its range (an expert never has more rows
 // than the batch has tokens).
+// split: contraction slices for the shared segment's 64-row tiles, with sh_part
+// the float32 partial-sum region (used when a slice count is above 1).
 moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh,
-                      hipStream_t st, bool marks) {
+                      hipStream_t st, bool marks, SharedSplit split = SharedSplit{},
+                      float* sh_part = nullptr) {
   // the tile path covers bf16 and its tile shapes; everything else streams
   const bool tiles_ok = dtype == MOGE_BF16 && moge::tile_path_ok(d, routed.inter) &&
                         (!sh || moge::tile_path_ok(d, sh->inter));
@@ -238,13 +268,22 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
       a.thr_hi = rg.hi;
       if (!routed_here) a.n_exp = 0;
       moge::TileSeg b;
+      const int ks = gateup ? split.gu : split.dn;
+      const bool sliced = sh_here && !rg.big && ks > 1 && sh_part;
       if (sh_here) {
         b = tile_view(*sh, gateup);
         b.thr = rg.sh_lo;
         b.thr_hi = rg.sh_hi;
+        if (sliced) {
+          b.ksplit = ks;
+          b.part = sh_part;
+        }
       }
       CHECK(hip_check(moge::launch_ffn_tile(gateup, rg.big, d, a, sh_here ? &b : nullptr, st),
                       gateup ? "expert gate/up tiles" : "expert down tiles"));
+      if (sliced && gateup)
+        CHECK(hip_check(moge::launch_swiglu_parts(sh_part, ks, sh->rows, sh->inter, sh->h, st),
+                        "shared SwiGLU of the slices"));
     }
     if (marks) mark(gateup ? 4 : 5, st);
   }
@@ -367,13 +406,20 @@ moge_status_t layer_impl(const moge_dims_t* dims, const void* x, const void* w_r
     sh.h = at<char>(ws, p.hs);
     sh.y = at<char>(ws, p.sh);
   }
+  const SharedSplit split = w.w8 ? SharedSplit{} : shared_split(dims);
+  float* const sh_part = at<float>(ws, p.sh_part);
   if (w.w8)
     CHECK(run_ffn_w8(dims->d, routed, shared ? &sh : nullptr, st, true));
   else
-    CHECK(run_ffn(dims->dtype, dims->d, T, routed, shared ? &sh : nullptr, st, true));
-  // S7 combine
+    CHECK(run_ffn(dims->dtype, dims->d, T, routed, shared ? &sh : nullptr, st, true, split,
+                  sh_part));
+  // S7 combine (the shared term as the slices' partial sums when its down
+  // projection was split)
+  const bool dn_parts = shared && split.dn > 1;
   CHECK(hip_check(moge::launch_combine(dims->dtype, T, K, dims->d, routed.y, pair_row, gate,
-                                       shared ? sh.y : nullptr, y, st),
+                                       shared && !dn_parts ? sh.y : nullptr,
+                                       dn_parts ? sh_part : nullptr, dn_parts ? split.dn : 0, y,
+                                       st),
                   "combine"));
   mark(6, st);
   return ok();
@@ -495,7 +541,7 @@ moge_status_t moge_combine(const moge_dims_t* dims, const void* y_perm, const in
   if (dims->T == 0) return ok();
   hipStream_t st = static_cast<hipStream_t>(stream);
   CHECK(hip_check(moge::launch_combine(dims->dtype, dims->T, dims->M * dims->k_per_group, dims->d,
-                                       y_perm, pair_row, topk_gate, shared_out, y, st),
+                                       y_perm, pair_row, topk_gate, shared_out, nullptr, 0, y, st),
                   "moge_combine"));
   return ok();
 }

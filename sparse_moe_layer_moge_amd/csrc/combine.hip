@@ -1,6 +1,8 @@
 // Gate-weighted combine back to token order:
 //   y[t] = shared[t] + sum_k gate[t,k] * y_perm[pair_row[t*K + k]]
-// in float32, slots in order k = 0..K-1 (deterministic), rounded once.
+// in float32, slots in order k = 0..K-1 (deterministic), rounded once.  The shared
+// term is either the shared experts' output or the float32 partial sums of its
+// split contraction, added in slice order first.
 // Slots without a row (pair_row < 0, only for invalid routing input) add nothing.
 #include "moge_common.hpp"
 #include "moge_internal.hpp"
@@ -45,12 +47,22 @@ __global__ __launch_bounds__(64) void k_combine(int T, int K, int d, int R,
                                                 const E* __restrict__ y_perm,
                                                 const int32_t* __restrict__ pair_row,
                                                 const float* __restrict__ gate,
-                                                const E* __restrict__ shared, E* __restrict__ y) {
+                                                const E* __restrict__ shared,
+                                                const float* __restrict__ shared_part,
+                                                int n_part, E* __restrict__ y) {
   const int t = blockIdx.x;
   const int c = blockIdx.y * 64 + threadIdx.x;
   if (c >= d / 8) return;
   float acc[8];
-  if (shared) {
+  if (shared_part) {
+    Vec8Io<float>::load(shared_part + (size_t)t * d + c * 8, acc);
+    for (int p = 1; p < n_part; ++p) {
+      float v[8];
+      Vec8Io<float>::load(shared_part + ((size_t)p * T + t) * d + c * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+  } else if (shared) {
     Vec8Io<E>::load(shared + (size_t)t * d + c * 8, acc);
   } else {
 #pragma unroll
@@ -86,16 +98,53 @@ __global__ __launch_bounds__(64) void k_combine(int T, int K, int d, int R,
 
 hipError_t launch_combine(int dtype, int T, int K, int d, const void* y_perm,
                           const int32_t* pair_row, const float* gate, const void* shared,
-                          void* y, hipStream_t st) {
+                          const float* shared_part, int n_part, void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const int R = T * K;
   dim3 grid(T, (d / 8 + 63) / 64);
   if (dtype == 1)
     hipLaunchKernelGGL(k_combine<bf16>, grid, dim3(64), 0, st, T, K, d, R, (const bf16*)y_perm,
-                       pair_row, gate, (const bf16*)shared, (bf16*)y);
+                       pair_row, gate, (const bf16*)shared, shared_part, n_part, (bf16*)y);
   else
     hipLaunchKernelGGL(k_combine<float>, grid, dim3(64), 0, st, T, K, d, R, (const float*)y_perm,
-                       pair_row, gate, (const float*)shared, (float*)y);
+                       pair_row, gate, (const float*)shared, shared_part, n_part, (float*)y);
+  return hipGetLastError();
+}
+
+// H[r, f] = silu(sum_s g[s][r][f]) * sum_s u[s][r][f] (slices in order), rounded to
+// bf16 once; g = part, u = part + ksplit * rows * inter.  One thread per 8 features.
+__global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ part, int ksplit,
+                                                      int rows, int inter, bf16* __restrict__ h) {
+  const size_t n8 = (size_t)rows * inter / 8;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const size_t plane = (size_t)rows * inter;
+  const float* up = part + (size_t)ksplit * plane;
+  float g[8], u[8];
+  Vec8Io<float>::load(part + i * 8, g);
+  Vec8Io<float>::load(up + i * 8, u);
+  for (int s = 1; s < ksplit; ++s) {
+    float a[8], b[8];
+    Vec8Io<float>::load(part + s * plane + i * 8, a);
+    Vec8Io<float>::load(up + s * plane + i * 8, b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      g[j] += a[j];
+      u[j] += b[j];
+    }
+  }
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = silu(g[j]) * u[j];
+  Vec8Io<bf16>::store(h + i * 8, v);
+}
+
+hipError_t launch_swiglu_parts(const float* part, int ksplit, int rows, int inter, void* h,
+                               hipStream_t st) {
+  const size_t n8 = (size_t)rows * inter / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_swiglu_parts, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, part,
+                     ksplit, rows, inter, (bf16*)h);
   return hipGetLastError();
 }
 

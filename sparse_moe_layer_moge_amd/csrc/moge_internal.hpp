@@ -116,12 +116,26 @@ struct TileSeg {
   const void* w1 = nullptr;        // row-major: up (gate/up)
   const void* packed = nullptr;    // packed part (expert-strided), or nullptr
   void* out = nullptr;             // H (gate/up) or y (down)
+  // Contraction split (64-row tiles only): with ksplit > 1 each tile computes
+  // 1/ksplit of the contraction and writes float32 partial sums to `part` instead
+  // of `out`: [ksplit][rows][d] for down; for gate/up the gate sums
+  // [ksplit][rows][inter] followed by the up sums in the same shape.
+  int ksplit = 1;
+  float* part = nullptr;
 };
 // big: 256-row tiles; otherwise 64-row tiles
 hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const TileSeg* b,
                            hipStream_t st);
 // shapes the tile kernels cover (96-feature gate/up tiles, 256-column down tiles)
 bool tile_path_ok(int d, int inter);
+// Contraction slices for a single segment of `rows` rows on the 64-row tiles with
+// contraction K and `col_tiles` weight tiles per row tile: enough tiles to cover
+// the CUs (planned for 256 of them), at least 12 stages of 64 per slice.  1 = no
+// split.  Depends on the sizes only.
+int tile_ksplit(int rows, int K, int col_tiles);
+// H = silu(sum of gate partials) * (sum of up partials), slices added in order, bf16
+hipError_t launch_swiglu_parts(const float* part, int ksplit, int rows, int inter, void* h,
+                               hipStream_t st);
 
 // ---- weight packing (pack.hip) --------------------------------------------
 // src1 != nullptr: gate/up pair [n_exp, rows, K] each; else down [n_exp, rows, K]
@@ -129,8 +143,10 @@ hipError_t launch_pack(int dtype, const void* src0, const void* src1, int n_exp,
                        void* dst, hipStream_t st);
 
 // ---- combine (combine.hip) -------------------------------------------------
+// shared_part (optional, instead of `shared`): n_part float32 partial sums
+// [n_part][T][d] of the shared experts' output, added in slice order
 hipError_t launch_combine(int dtype, int T, int K, int d, const void* y_perm,
                           const int32_t* pair_row, const float* gate, const void* shared,
-                          void* y, hipStream_t st);
+                          const float* shared_part, int n_part, void* y, hipStream_t st);
 
 }  // namespace moge

@@ -200,8 +200,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
   // ---- the tile lists (every wave computes the totals) -----------------------
-  const int nta = GATEUP ? a.inter / S::kFeat : d / S::kWRows;
-  const int ntb = b.n_exp ? (GATEUP ? b.inter / S::kFeat : d / S::kWRows) : 0;
+  // entries per row tile: weight tiles times contraction slices (slice-major)
+  const int nta = (GATEUP ? a.inter / S::kFeat : d / S::kWRows) * (BIG ? 1 : a.ksplit);
+  const int ntb = b.n_exp ? (GATEUP ? b.inter / S::kFeat : d / S::kWRows) * (BIG ? 1 : b.ksplit) : 0;
   const int ma = seg_total_tiles<S::kM>(a);
   const int mb = b.n_exp ? seg_total_tiles<S::kM>(b) : 0;
   // every XCD takes an equal share of each segment; the segment with the longer
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   const int x = blockIdx.x % kXcds;
   auto run_tile = [&](int it) {
   if (w == 0) {
-    int seg = -1, e = 0, row0 = 0, rows = 0, nt = 0;
+    int seg = -1, e = 0, row0 = 0, rows = 0, nt = 0, ks = 0;
     int which = -1, t = 0;
     if (it < ch0) {
       t = x * ch0 + it;
@@ -229,7 +230,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       seg = (which == 0) == b_first ? 1 : 0;
       const TileSeg& g = seg ? b : a;
       const int ntg = seg ? ntb : nta;
+      const int ntc = ntg / (BIG ? 1 : g.ksplit);  // weight tiles per row tile
       nt = t % ntg;
+      ks = nt / ntc;
+      nt -= ks * ntc;
       if (!seg_find_tile<S::kM>(g, t / ntg, &e, &row0, &rows) || rows <= 0) seg = -1;
     }
     if (l == 0) {
@@ -238,6 +242,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       s_tile[2] = row0;
       s_tile[3] = rows;
       s_tile[4] = nt;
+      s_tile[5] = ks;
     }
   }
   __syncthreads();
@@ -247,8 +252,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   const int e = s_tile[1];
   const int row0 = s_tile[2], rows = s_tile[3];
   const int nt = s_tile[4];
+  // contraction slices exist for the small shape only
+  const int kslice = BIG ? 0 : s_tile[5];
   const int K = GATEUP ? d : g.inter;              // contraction length of this segment
-  const int nk = K / kTileK;                       // stages
+  const int nk = K / kTileK / (BIG ? 1 : g.ksplit);  // stages of this tile's slice
+  const int kb0 = kslice * nk;                     // its first stage
 
   // LDS byte address of the buffers; the wave index as a scalar (every load below
   // has a wave-uniform destination)
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
     const int r = (wu * S::kALoads + i) * kRowsPerLoad + lr;
     const int rr = row0 + min(r, rows - 1);
     const int src = (GATEUP && g.row_src) ? g.row_src[rr] / g.row_div : rr;
-    a_voff[i] = (uint32_t)(((size_t)src * K + swz_chunk(r, l & 7) * 8) * sizeof(E));
+    a_voff[i] = (uint32_t)(((size_t)src * K + kb0 * kTileK + swz_chunk(r, l & 7) * 8) * sizeof(E));
   }
   // ---- B: the stage's weight rows in MFMA fragment order: fragment f = 2 rb + kh
   // holds rows 16 rb .. +15 and elements 32 kh .. +31 of the stage, lane j of the
@@ -296,12 +304,13 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
     const int rb = f >> 1, kh = f & 1;
     const int blk = rb >> 1, half = rb & 1;
     if (packed) {
-      // packed block pb: step j of 32 elements holds tiles 2j (half 0), 2j + 1 (half 1)
+      // packed block pb: step j of 32 elements holds tiles 2j (half 0), 2j + 1 (half 1);
+      // a block has 2 * (K / 32) tiles, the slice starts at step 2 * kb0
       const int pb = nt * S::kBlocksPerTile + blk;
-      b_voff[i] = (uint32_t)((pb * nk * 4 + kh * 2 + half) * tb + l * 16);
+      b_voff[i] = (uint32_t)(((pb * (K / kTileK) + kb0) * 4 + kh * 2 + half) * tb + l * 16);
     } else {
       const int row = GATEUP ? nt * S::kFeat + blk * 16 + (l & 15) : nt * S::kWRows + rb * 16 + (l & 15);
-      b_voff[i] = (uint32_t)(((size_t)row * K + kh * 32 + (l >> 4) * 8) * sizeof(E));
+      b_voff[i] = (uint32_t)(((size_t)row * K + kb0 * kTileK + kh * 32 + (l >> 4) * 8) * sizeof(E));
     }
   }
   // row-major gate/up: odd row blocks are up rows
@@ -444,8 +453,40 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   // instruction.  An LDS row holds kNCp chunk slots (kNC used); chunk c of tile row
   // r sits at slot c ^ (r % kNCp), which keeps the scattered writes free of bank
   // conflicts.  Gate/up first applies SwiGLU in registers.
-  E* out = static_cast<E*>(g.out);
   constexpr int kOutCols = GATEUP ? S::kFeat : S::kWRows;   // output columns per tile
+  if (!BIG && g.ksplit > 1) {
+    // float32 partial sums straight from the accumulators: register group gq of
+    // block q is 4 consecutive columns (down) or features (gate/up: registers
+    // 4 gq .. +3 gate, 4 gq + 8 .. +11 up) of tile row 32 (kTP wm + p) + l % 32
+    const int ld = GATEUP ? g.inter : d;
+    const size_t plane = (size_t)g.rows * ld;
+    float* const pg = g.part + kslice * plane;
+    float* const pu = g.part + (size_t)g.ksplit * plane + kslice * plane;
+#pragma unroll
+    for (int p = 0; p < kTP; ++p) {
+      const int r = (wm * kTP + p) * 32 + (l & 31);
+      if (r < rows) {
+#pragma unroll
+        for (int q = 0; q < kWP; ++q) {
+#pragma unroll
+          for (int gq = 0; gq < (GATEUP ? 2 : 4); ++gq) {
+            const int col = nt * kOutCols + (wn * kWP + q) * (GATEUP ? 16 : 32) + 8 * gq + 4 * (l >> 5);
+            const size_t o = (size_t)(row0 + r) * ld + col;
+            f32x4 v;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = acc[q][p][gq * 4 + k];
+            *reinterpret_cast<f32x4*>(pg + o) = v;
+            if (GATEUP) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) v[k] = acc[q][p][gq * 4 + 8 + k];
+              *reinterpret_cast<f32x4*>(pu + o) = v;
+            }
+          }
+        }
+      }
+    }
+  } else {
+  E* out = static_cast<E*>(g.out);
   constexpr int kNC = kOutCols * (int)sizeof(E) / 16;        // 16-byte chunks per row
   constexpr int kNCp = kNC <= 8 ? 8 : kNC <= 16 ? 16 : 32;   // ... rounded up to 2^k
   constexpr int kPitch = kNCp * 16;
@@ -476,6 +517,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
     const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * kPitch + ((c ^ (r & (kNCp - 1))) << 4));
     *reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * ld + col0 + c * 8) = v;
   }
+  }  // ksplit
   }  // seg >= 0
   };
   if constexpr (BIG) {
@@ -519,8 +561,8 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
   typedef TileShape<GATEUP, BIG> S;
   const TileSeg bb = b ? *b : TileSeg{};
   const long long wa = GATEUP ? S::kFeat : S::kWRows;
-  const long long nta = GATEUP ? a.inter / wa : d / wa;
-  const long long ntb = b ? (GATEUP ? bb.inter / wa : d / wa) : 0;
+  const long long nta = (GATEUP ? a.inter / wa : d / wa) * a.ksplit;
+  const long long ntb = b ? (GATEUP ? bb.inter / wa : d / wa) * bb.ksplit : 0;
   // each segment's tiles are spread over the XCDs separately
   const long long ba = tile_bound(a, S::kM) * nta, bbn = tile_bound(bb, S::kM) * ntb;
   long long per_xcd = (ba + kXcds - 1) / kXcds + (bbn + kXcds - 1) / kXcds;
@@ -539,8 +581,20 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
   return hipGetLastError();
 }
 
+int tile_ksplit(int rows, int K, int col_tiles) {
+  constexpr int kPlanCUs = 256;   // MI355X; the split depends on the sizes only
+  const int nk = K / kTileK;
+  const long long tiles = (long long)((rows + 63) / 64) * col_tiles;
+  int best = 1;   // the most slices that still fit one round of workgroups
+  for (int ks = 2; ks <= 8; ++ks)
+    if (nk % ks == 0 && nk / ks >= 12 && tiles * ks <= kPlanCUs) best = ks;
+  return best;
+}
+
 hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const TileSeg* b,
                            hipStream_t st) {
+  // contraction slices are a 64-row-tile feature
+  if (big && (a.ksplit > 1 || (b && b->ksplit > 1))) return hipErrorInvalidValue;
   if (gateup) return big ? launch_shape<true, true>(d, a, b, st) : launch_shape<true, false>(d, a, b, st);
   return big ? launch_shape<false, true>(d, a, b, st) : launch_shape<false, false>(d, a, b, st);
 }

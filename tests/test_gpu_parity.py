@@ -401,8 +401,9 @@ def test_layer_one_expert_per_group_takes_everything(lib, name, T):
     assert normwise_rel_err(values(out["y"])[tok], ref["y"]) <= tolerance(cfg)
 
 
-@pytest.mark.parametrize("name,T", [("C0", 64), ("C1", 64), ("C2", 456)])
-def test_layer_deterministic_and_equal_to_step_path(lib, name, T):
+@pytest.mark.parametrize("name,T,split_shared", [("C0", 64, False), ("C1", 64, True),
+                                                 ("C1", 17, False), ("C2", 456, False)])
+def test_layer_deterministic_and_equal_to_step_path(lib, name, T, split_shared):
     import torch
     cfg = CONFIGS[name]
     inp, dw = layer_inputs(cfg, T)
@@ -436,4 +437,11 @@ def test_layer_deterministic_and_equal_to_step_path(lib, name, T):
     y = _empty((T, cfg.d), dw["x"].dtype)
     lib.combine(dims, y_perm, pr, gate, sh, y)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(to_host(y), a["y"])
+    if split_shared:
+        # the layer splits the shared experts' contraction over several 64-row tiles
+        # and adds the float32 partial sums without the step path's bf16 rounding of
+        # H_s and of the shared output: the results differ by those roundings
+        err = normwise_rel_err(values(to_host(y)), values(a["y"]))
+        assert 0 < err <= 2 * 2.0 ** -8, err
+    else:
+        np.testing.assert_array_equal(to_host(y), a["y"])
