@@ -210,10 +210,12 @@ moge_status_t moge_layer_forward_packed(const moge_dims_t* dims, const void* x,
  * the weight half: every row of W_gate, W_up, W_down and of the shared experts'
  * weights holds int8 codes q with one float32 scale s, weight = s * q; activations,
  * H and the outputs stay bf16.  At decode batch sizes the layer streams its expert
- * weights from HBM, so one byte per weight halves the dominant stream.  Every
- * expert takes the streaming kernels whatever its row count: the int8 layer is
- * meant for decode batches (up to about 64 rows per expert); prefill belongs to
- * the bf16 packed layer.
+ * weights from HBM, so one byte per weight halves the dominant stream.  Experts
+ * with at most 32 rows stream their codes; larger ones (and the shared experts
+ * of a batch above 32 tokens) take 64-row MFMA tiles that widen the codes from
+ * LDS.  The int8 layer is meant for decode and mid-size batches; prefill batches,
+ * where the matrix cores and not the weight stream set the time, belong to the
+ * bf16 packed layer.
  * Requirements: dtype MOGE_BF16; d, inter and shared_inter multiples of 64
  * (MOGE_ERR_UNSUPPORTED otherwise).
  *

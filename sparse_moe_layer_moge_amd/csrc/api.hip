@@ -138,13 +138,29 @@ bool tiles_ok_for(const moge_dims_t* d) {
          (d->shared_inter == 0 || moge::tile_path_ok(d->d, d->shared_inter));
 }
 
-SharedSplit shared_split(const moge_dims_t* d) {
+bool w8_tiles_ok_for(const moge_dims_t* d) {
+  return moge::tile_path_w8_ok(d->d, d->inter) &&
+         (d->shared_inter == 0 || moge::tile_path_w8_ok(d->d, d->shared_inter));
+}
+
+// w8: the int8 layer, whose shared segment takes 64-row tiles at every size above
+// the streaming limit
+SharedSplit shared_split(const moge_dims_t* d, bool w8) {
   SharedSplit s;
   const int T = d->T, Is = d->shared_inter;
-  if (Is == 0 || !tiles_ok_for(d) || T <= moge::kSharedStreamMaxRows) return s;
-  if (T <= moge::kSharedSmallGateUpRows) s.gu = moge::tile_ksplit(T, d->d, Is / 64);
-  if (T <= moge::kSharedSmallDownRows) s.dn = moge::tile_ksplit(T, Is, d->d / 128);
+  if (Is == 0 || T <= moge::kSharedStreamMaxRows) return s;
+  if (w8 ? !w8_tiles_ok_for(d) : !tiles_ok_for(d)) return s;
+  if (w8 || T <= moge::kSharedSmallGateUpRows) s.gu = moge::tile_ksplit(T, d->d, Is / 64);
+  if (w8 || T <= moge::kSharedSmallDownRows) s.dn = moge::tile_ksplit(T, Is, d->d / 128);
   return s;
+}
+
+// float32 partial-sum bytes a split needs (gate/up and down use it in turn)
+size_t split_part_bytes(const moge_dims_t* d, const SharedSplit& ss) {
+  size_t part = 0;
+  if (ss.gu > 1) part = (size_t)2 * ss.gu * d->T * d->shared_inter * 4;
+  if (ss.dn > 1 && (size_t)ss.dn * d->T * d->d * 4 > part) part = (size_t)ss.dn * d->T * d->d * 4;
+  return part;
 }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -174,11 +190,10 @@ Plan make_plan(const moge_dims_t* d) {
   p.hs = take(T * (size_t)d->shared_inter * es);
   p.y_perm = take(R * (size_t)d->d * es);
   p.sh = take(T * (size_t)d->d * es);
-  const SharedSplit ss = shared_split(d);
-  size_t part = 0;
-  if (ss.gu > 1) part = (size_t)2 * ss.gu * T * d->shared_inter * 4;
-  if (ss.dn > 1 && (size_t)ss.dn * T * d->d * 4 > part) part = (size_t)ss.dn * T * d->d * 4;
-  p.sh_part = take(part);
+  // the bf16 and the int8 layer share the workspace layout
+  const size_t part_bf16 = split_part_bytes(d, shared_split(d, false));
+  const size_t part_w8 = d->dtype == MOGE_BF16 ? split_part_bytes(d, shared_split(d, true)) : 0;
+  p.sh_part = take(part_bf16 > part_w8 ? part_bf16 : part_w8);
   p.total = o;
   return p;
 }
@@ -290,16 +305,58 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
   return MOGE_OK;
 }
 
-// Weight-only int8 experts: every expert streams its codes whatever its row count
-// (the MFMA tile kernels take bf16 weights only).
-moge_status_t run_ffn_w8(int d, moge::FfnSeg& routed, moge::FfnSeg* sh, hipStream_t st,
-                         bool marks) {
-  routed.thr = INT_MAX;
-  if (sh) sh->thr = INT_MAX;
-  CHECK(hip_check(moge::launch_ffn_gateup_w8(d, routed, sh, st), "int8 expert gate/up"));
-  if (marks) mark(4, st);
-  CHECK(hip_check(moge::launch_ffn_down_w8(d, routed, sh, st), "int8 expert down"));
-  if (marks) mark(5, st);
+// The tile-path view of an int8 segment: code tiles and row scales.
+moge::TileSeg tile_view_w8(const moge::FfnSeg& f, bool gateup) {
+  moge::TileSeg t = tile_view(f, gateup);
+  t.packed = gateup ? f.p_gu : f.p_down;
+  t.sc0 = gateup ? f.sc_gate : f.sc_down;
+  t.sc1 = gateup ? f.sc_up : nullptr;
+  return t;
+}
+
+// Weight-only int8 experts: experts with at most kStreamMaxRows rows (the shared
+// segment: kSharedStreamMaxRows) stream their codes; larger ones take the int8
+// 64-row tiles, the shared segment with its contraction split when it is small.
+// Without a tile shape for the sizes every expert streams.
+moge_status_t run_ffn_w8(int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh, hipStream_t st,
+                         bool marks, SharedSplit split, float* sh_part) {
+  const bool tiles = moge::tile_path_w8_ok(d, routed.inter) &&
+                     (!sh || moge::tile_path_w8_ok(d, sh->inter));
+  routed.thr = tiles ? moge::kStreamMaxRows : INT_MAX;
+  if (sh) sh->thr = tiles ? moge::kSharedStreamMaxRows : INT_MAX;
+  const bool sh_stream = sh && sh->rows <= sh->thr;
+  for (int gateup = 1; gateup >= 0; --gateup) {
+    if (gateup)
+      CHECK(hip_check(moge::launch_ffn_gateup_w8(d, routed, sh_stream ? sh : nullptr, st),
+                      "int8 expert gate/up"));
+    else
+      CHECK(hip_check(moge::launch_ffn_down_w8(d, routed, sh_stream ? sh : nullptr, st),
+                      "int8 expert down"));
+    const bool routed_here = tiles && T > routed.thr;
+    const bool sh_here = tiles && sh && !sh_stream;
+    if (routed_here || sh_here) {
+      moge::TileSeg a = tile_view_w8(routed, gateup);
+      a.thr = routed.thr;
+      if (!routed_here) a.n_exp = 0;
+      moge::TileSeg b;
+      const int ks = gateup ? split.gu : split.dn;
+      const bool sliced = sh_here && ks > 1 && sh_part;
+      if (sh_here) {
+        b = tile_view_w8(*sh, gateup);
+        b.thr = sh->thr;
+        if (sliced) {
+          b.ksplit = ks;
+          b.part = sh_part;
+        }
+      }
+      CHECK(hip_check(moge::launch_ffn_tile_w8(gateup, d, a, sh_here ? &b : nullptr, st),
+                      gateup ? "int8 expert gate/up tiles" : "int8 expert down tiles"));
+      if (sliced && gateup)
+        CHECK(hip_check(moge::launch_swiglu_parts(sh_part, ks, sh->rows, sh->inter, sh->h, st),
+                        "shared SwiGLU of the slices"));
+    }
+    if (marks) mark(gateup ? 4 : 5, st);
+  }
   return MOGE_OK;
 }
 
@@ -406,10 +463,10 @@ moge_status_t layer_impl(const moge_dims_t* dims, const void* x, const void* w_r
     sh.h = at<char>(ws, p.hs);
     sh.y = at<char>(ws, p.sh);
   }
-  const SharedSplit split = w.w8 ? SharedSplit{} : shared_split(dims);
+  const SharedSplit split = shared_split(dims, w.w8);
   float* const sh_part = at<float>(ws, p.sh_part);
   if (w.w8)
-    CHECK(run_ffn_w8(dims->d, routed, shared ? &sh : nullptr, st, true));
+    CHECK(run_ffn_w8(dims->d, T, routed, shared ? &sh : nullptr, st, true, split, sh_part));
   else
     CHECK(run_ffn(dims->dtype, dims->d, T, routed, shared ? &sh : nullptr, st, true, split,
                   sh_part));

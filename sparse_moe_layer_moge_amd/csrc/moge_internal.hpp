@@ -122,12 +122,21 @@ struct TileSeg {
   // [ksplit][rows][inter] followed by the up sums in the same shape.
   int ksplit = 1;
   float* part = nullptr;
+  // int8 codes (launch_ffn_tile_w8): `packed` holds the code tiles, sc0 the row
+  // scales of the gate rows [n_exp, inter] (down: of the output columns
+  // [n_exp, d]) and sc1 those of the up rows
+  const float* sc0 = nullptr;
+  const float* sc1 = nullptr;
 };
 // big: 256-row tiles; otherwise 64-row tiles
 hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const TileSeg* b,
                            hipStream_t st);
 // shapes the tile kernels cover (96-feature gate/up tiles, 256-column down tiles)
 bool tile_path_ok(int d, int inter);
+// 64-row tiles on int8 codes (tiles from `thr` rows up), and the shapes they cover
+hipError_t launch_ffn_tile_w8(bool gateup, int d, const TileSeg& a, const TileSeg* b,
+                              hipStream_t st);
+bool tile_path_w8_ok(int d, int inter);
 // Contraction slices for a single segment of `rows` rows on the 64-row tiles with
 // contraction K and `col_tiles` weight tiles per row tile: enough tiles to cover
 // the CUs (planned for 256 of them), at least 12 stages of 64 per slice.  1 = no

@@ -43,6 +43,7 @@
 #include "moge_common.hpp"
 #include "moge_internal.hpp"
 #include "packed_layout.hpp"
+#include "w8_layout.hpp"
 
 namespace moge {
 
@@ -53,7 +54,8 @@ constexpr int kXcds = 8;
 constexpr int kRowsPerLoad = 8;         // A rows one wave instruction moves
 constexpr int kFragBytes = 1024;        // one 16 x 32 bf16 MFMA fragment
 
-template <bool GATEUP, bool BIG> struct TileShape {
+// W8: int8 weight codes (w8_layout.hpp) instead of bf16 weights, small shape only.
+template <bool GATEUP, bool BIG, bool W8 = false> struct TileShape {
   static constexpr int kM = BIG ? 256 : 64;                       // rows per tile
   static constexpr int kWRows = BIG ? (GATEUP ? 192 : 256) : 128;  // weight rows per tile
   static constexpr int kFeat = kWRows / 2;                         // gate/up features per tile
@@ -65,7 +67,9 @@ template <bool GATEUP, bool BIG> struct TileShape {
   static constexpr int kDA = BIG ? 2 : 6;                          // activation stages in LDS
   static constexpr int kDB = BIG ? 3 : 6;                          // weight stages in LDS
   static constexpr int kAStageBytes = kM * kLineBytes;
-  static constexpr int kBStageBytes = kWRows * kLineBytes;         // kWRows / 8 fragments
+  // B stage: bf16 weights, kWRows / 8 fragments of 1 KiB; int8 codes, kWRows / 16
+  // code tiles of 1 KiB (16 rows x 64 codes)
+  static constexpr int kBStageBytes = kWRows * kTileK * (W8 ? 1 : 2);
   static constexpr int kLdsBytes = kDA * kAStageBytes + kDB * kBStageBytes;
   // wave instructions per stage: A (8 rows each), B (one fragment each)
   static constexpr int kALoads = kM / kRowsPerLoad / 4;
@@ -76,7 +80,21 @@ template <bool GATEUP, bool BIG> struct TileShape {
   static_assert(kWP * kWavesN == kBlocksPerTile && kTP >= 1, "wave layout");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   static_assert((kALoads + kBLoads) * kEvery <= 4 * kTP * kWP, "loads must fit in a stage");
+  static_assert(!(W8 && BIG), "int8 codes use the small shape");
 };
+
+// 8 int8 codes -> their bf16 values (exact: at most 8 significant bits)
+__device__ __forceinline__ bf16x8 widen8(uint64_t c) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = (float)(int8_t)((c >> (16 * j)) & 0xffu);
+    const float b = (float)(int8_t)((c >> (16 * j + 8)) & 0xffu);
+    o[j] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a),
+                                 0x07060302u);
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+}
 
 // One wave instruction: 64 lanes x 16 bytes from a buffer straight into LDS at
 // byte address `m0v` + 16 * lane (m0v wave-uniform).  Written as inline asm so that
@@ -185,10 +203,10 @@ template <int kM> __device__ __forceinline__ int seg_total_tiles(const TileSeg& 
   return s;
 }
 
-template <bool GATEUP, bool BIG>
+template <bool GATEUP, bool BIG, bool W8>
 __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
   typedef bf16 E;
-  typedef TileShape<GATEUP, BIG> S;
+  typedef TileShape<GATEUP, BIG, W8> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::kLdsBytes];
   char* const ldsA = lds;
   char* const ldsB = lds + S::kDA * S::kAStageBytes;
@@ -283,9 +301,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   // 1 KiB read.  Row block rb is half rb % 2 of 32-row block rb / 2: for gate/up the
   // gate (half 0) or up rows of features kFeat nt + 16 (rb / 2) .. +15; for down,
   // output columns kWRows nt + 16 rb .. +15.
-  const bool packed = g.packed != nullptr;
+  const bool packed = W8 || g.packed != nullptr;
   Rsrc br0, br1;
-  if (GATEUP) {
+  if (W8) {
+    // int8 codes: gate/up part 2 * inter * d bytes per expert, down part d * inter
+    const size_t eb = GATEUP ? (size_t)2 * g.inter * d : (size_t)d * g.inter;
+    br0 = make_rsrc(static_cast<const char*>(g.packed) + e * eb, eb);
+    br1 = br0;
+  } else if (GATEUP) {
     const size_t ee = (size_t)g.inter * d;
     br0 = packed ? make_rsrc(static_cast<const char*>(g.packed) + e * 2 * ee * sizeof(E), 2 * ee * sizeof(E))
                  : make_rsrc(static_cast<const E*>(g.w0) + e * ee, ee * sizeof(E));
@@ -303,7 +326,12 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
     const int f = wu * S::kBLoads + i;
     const int rb = f >> 1, kh = f & 1;
     const int blk = rb >> 1, half = rb & 1;
-    if (packed) {
+    if (W8) {
+      // code tiles of block pb: step j of 64 codes holds tiles 2j (half 0) and 2j + 1;
+      // one stage is one step, so the wave's load i is code tile rb = f of the stage
+      const int pb = nt * S::kBlocksPerTile + ((f >> 1));
+      b_voff[i] = (uint32_t)(((pb * (K / kTileK) + kb0) * 2 + (f & 1)) * kW8TileBytes + l * 16);
+    } else if (packed) {
       // packed block pb: step j of 32 elements holds tiles 2j (half 0), 2j + 1 (half 1);
       // a block has 2 * (K / 32) tiles, the slice starts at step 2 * kb0
       const int pb = nt * S::kBlocksPerTile + blk;
@@ -318,8 +346,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
     const int f = wu * S::kBLoads + i;
     return (GATEUP && ((f >> 1) & 1)) ? br1 : br0;
   };
-  // per stage: packed weights advance 2 steps of (2 tiles), row-major 64 elements
-  const uint32_t b_step = packed ? 4 * tb : kLineBytes;
+  // per stage: packed weights advance 2 steps of (2 tiles), codes 1 step of 2 code
+  // tiles, row-major weights 64 elements
+  const uint32_t b_step = W8 ? 2 * kW8TileBytes : packed ? 4 * tb : kLineBytes;
   const uint32_t a_step = kLineBytes;
 
   // wave load i of the A rows of stage s, and of the B rows
@@ -357,8 +386,17 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
     const int off = lane_row + (((2 * h + (l >> 5)) ^ lswz) << 4);
     const int boff = bhalf + (h >> 1) * kFragBytes + ((2 * (h & 1) + (l >> 5)) * 16 + (l & 15)) * 16;
 #pragma unroll
-    for (int q = 0; q < kWP; ++q)
-      wf[q] = *reinterpret_cast<const bf16x8*>(B + (wn * kWP + q) * 4 * kFragBytes + boff);
+    for (int q = 0; q < kWP; ++q) {
+      if (W8) {
+        // code tile 2 (32-row block) + (l % 32) / 16, chunk 16 h + l % 16 (row l % 16,
+        // codes 16 h .. +15 of the stage), codes 8 (l / 32) .. +7 of the chunk
+        const char* cp = B + (2 * (wn * kWP + q) + ((l & 31) >> 4)) * kW8TileBytes +
+                         (h * 16 + (l & 15)) * 16 + 8 * (l >> 5);
+        wf[q] = widen8(*reinterpret_cast<const uint64_t*>(cp));
+      } else {
+        wf[q] = *reinterpret_cast<const bf16x8*>(B + (wn * kWP + q) * 4 * kFragBytes + boff);
+      }
+    }
 #pragma unroll
     for (int p = 0; p < kTP; ++p)
       tf[p] = *reinterpret_cast<const bf16x8*>(A + (wm * kTP + p) * 32 * kLineBytes + off);
@@ -454,6 +492,29 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   // r sits at slot c ^ (r % kNCp), which keeps the scattered writes free of bank
   // conflicts.  Gate/up first applies SwiGLU in registers.
   constexpr int kOutCols = GATEUP ? S::kFeat : S::kWRows;   // output columns per tile
+  if constexpr (W8) {
+    // weight row scales: register group gq of block q is 4 consecutive rows
+    // (gate/up: gate rows 4 gq .. of the block's 16 features, registers + 8 the up
+    // rows of the same features; down: output columns)
+#pragma unroll
+    for (int q = 0; q < kWP; ++q) {
+      const int blk = wn * kWP + q;
+#pragma unroll
+      for (int gq = 0; gq < (GATEUP ? 2 : 4); ++gq) {
+        const int row = nt * kOutCols + blk * (GATEUP ? 16 : 32) + 8 * gq + 4 * (l >> 5);
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(g.sc0 + (size_t)e * (GATEUP ? g.inter : d) + row);
+        f32x4 s1 = s0;
+        if (GATEUP) s1 = *reinterpret_cast<const f32x4*>(g.sc1 + (size_t)e * g.inter + row);
+#pragma unroll
+        for (int p = 0; p < kTP; ++p)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            acc[q][p][gq * 4 + k] *= s0[k];
+            if (GATEUP) acc[q][p][gq * 4 + 8 + k] *= s1[k];
+          }
+      }
+    }
+  }
   if (!BIG && g.ksplit > 1) {
     // float32 partial sums straight from the accumulators: register group gq of
     // block q is 4 consecutive columns (down) or features (gate/up: registers
@@ -556,9 +617,9 @@ static long long tile_bound(const TileSeg& g, int kM) {
   return bound;
 }
 
-template <bool GATEUP, bool BIG>
+template <bool GATEUP, bool BIG, bool W8 = false>
 static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStream_t st) {
-  typedef TileShape<GATEUP, BIG> S;
+  typedef TileShape<GATEUP, BIG, W8> S;
   const TileSeg bb = b ? *b : TileSeg{};
   const long long wa = GATEUP ? S::kFeat : S::kWRows;
   const long long nta = (GATEUP ? a.inter / wa : d / wa) * a.ksplit;
@@ -576,7 +637,7 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
   }
   const long long grid = per_xcd * kXcds;
   if (grid > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG>), dim3((unsigned)grid), dim3(kTileThreads), 0, st,
+  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8>), dim3((unsigned)grid), dim3(kTileThreads), 0, st,
                      a, bb, d);
   return hipGetLastError();
 }
@@ -597,6 +658,18 @@ hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const
   if (big && (a.ksplit > 1 || (b && b->ksplit > 1))) return hipErrorInvalidValue;
   if (gateup) return big ? launch_shape<true, true>(d, a, b, st) : launch_shape<true, false>(d, a, b, st);
   return big ? launch_shape<false, true>(d, a, b, st) : launch_shape<false, false>(d, a, b, st);
+}
+
+bool tile_path_w8_ok(int d, int inter) {
+  // 64-feature gate/up and 128-column down tiles of 64-code stages
+  return d % TileShape<false, false, true>::kWRows == 0 && d % kW8Step == 0 &&
+         inter % TileShape<true, false, true>::kFeat == 0 && inter % kW8Step == 0;
+}
+
+hipError_t launch_ffn_tile_w8(bool gateup, int d, const TileSeg& a, const TileSeg* b,
+                              hipStream_t st) {
+  return gateup ? launch_shape<true, false, true>(d, a, b, st)
+                : launch_shape<false, false, true>(d, a, b, st);
 }
 
 }  // namespace moge
