@@ -39,11 +39,13 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_F32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CSRC = os.path.join(ROOT, "sparse_moe_layer_moge_amd", "csrc")
-# sources of the kernels behind the roofline line (a stored traffic figure is used
-# only while they are unchanged)
+# sources of the kernels behind the roofline line, and of the dispatch that picks
+# them (a stored traffic figure is used only while they are unchanged)
 FFN_SOURCES = {"bf16": ("ffn.hip", "ffn_rows.hpp", "stream_tile.hpp", "packed_layout.hpp",
-                        "tile_gemm.hip", "moge_common.hpp"),
-               "w8": ("ffn_w8.hip", "ffn_rows.hpp", "w8_layout.hpp", "moge_common.hpp")}
+                        "tile_gemm.hip", "combine.hip", "api.hip", "moge_internal.hpp",
+                        "moge_common.hpp"),
+               "w8": ("ffn_w8.hip", "ffn_rows.hpp", "w8_layout.hpp", "tile_gemm.hip",
+                      "combine.hip", "api.hip", "moge_internal.hpp", "moge_common.hpp")}
 
 
 def parse_args():
@@ -312,7 +314,9 @@ def main() -> int:
                    "shared_inter_total": cfg.I_s, "parallelism": "single GPU",
                    "weights": ("int8 codes, float32 per-row scales" if args.w8 else
                                "row-major" if args.row_major else "packed")},
-        "roofline": {"bound": bound, "kernel": "gate_up+SwiGLU (routed+shared)",
+        "roofline": {"bound": bound,
+                     "kernel": "gate/up + SwiGLU stage (routed and shared experts: every "
+                               "kernel between the two stage events)",
                      "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "algorithmic_bytes": work["gate_up"]["bytes"],
