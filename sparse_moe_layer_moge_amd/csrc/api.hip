@@ -150,8 +150,16 @@ SharedSplit shared_split(const moge_dims_t* d, bool w8) {
   const int T = d->T, Is = d->shared_inter;
   if (Is == 0 || T <= moge::kSharedStreamMaxRows) return s;
   if (w8 ? !w8_tiles_ok_for(d) : !tiles_ok_for(d)) return s;
-  if (w8 || T <= moge::kSharedSmallGateUpRows) s.gu = moge::tile_ksplit(T, d->d, Is / 64);
-  if (w8 || T <= moge::kSharedSmallDownRows) s.dn = moge::tile_ksplit(T, Is, d->d / 128);
+  // 64-row tiles: 64 features (gate/up) or 128 columns (down) per tile; 256-row
+  // tiles: 96 features or 256 columns
+  if (w8 || T <= moge::kSharedSmallGateUpRows)
+    s.gu = moge::tile_ksplit(T, d->d, Is / 64, 64);
+  else
+    s.gu = moge::tile_ksplit(T, d->d, Is / 96, 256);
+  if (w8 || T <= moge::kSharedSmallDownRows)
+    s.dn = moge::tile_ksplit(T, Is, d->d / 128, 64);
+  else
+    s.dn = moge::tile_ksplit(T, Is, d->d / 256, 256);
   return s;
 }
 
@@ -284,7 +292,7 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
       if (!routed_here) a.n_exp = 0;
       moge::TileSeg b;
       const int ks = gateup ? split.gu : split.dn;
-      const bool sliced = sh_here && !rg.big && ks > 1 && sh_part;
+      const bool sliced = sh_here && ks > 1 && sh_part;
       if (sh_here) {
         b = tile_view(*sh, gateup);
         b.thr = rg.sh_lo;
@@ -294,8 +302,16 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
           b.part = sh_part;
         }
       }
-      CHECK(hip_check(moge::launch_ffn_tile(gateup, rg.big, d, a, sh_here ? &b : nullptr, st),
-                      gateup ? "expert gate/up tiles" : "expert down tiles"));
+      const char* what = gateup ? "expert gate/up tiles" : "expert down tiles";
+      if (sliced && rg.big) {
+        // sliced 256-row tiles are an instantiation of their own: the routed
+        // experts of this range go in a plain launch first
+        if (routed_here) CHECK(hip_check(moge::launch_ffn_tile(gateup, true, d, a, nullptr, st), what));
+        CHECK(hip_check(moge::launch_ffn_tile(gateup, true, d, b, nullptr, st), what));
+      } else {
+        CHECK(hip_check(moge::launch_ffn_tile(gateup, rg.big, d, a, sh_here ? &b : nullptr, st),
+                        what));
+      }
       if (sliced && gateup)
         CHECK(hip_check(moge::launch_swiglu_parts(sh_part, ks, sh->rows, sh->inter, sh->h, st),
                         "shared SwiGLU of the slices"));

@@ -89,10 +89,9 @@ hipError_t launch_w8_quantize(const void* src0, const void* src1, int n_exp, int
 // with more take 64-row MFMA tiles up to kSmallTileMaxRows rows and 256-row tiles
 // beyond.  The shared experts (one segment of T rows) stream up to
 // kSharedStreamMaxRows and take 64-row tiles up to kSharedSmallGateUpRows (gate/up)
-// or kSharedSmallDownRows (down): a single segment of a few hundred rows has too
-// few 256-row tiles to fill the CUs (the down projection, with 256 output columns
-// per tile, far fewer than gate/up), while in the launch of the routed experts it
-// shares them.  A streamed segment of more than 32 rows keeps three or four row
+// or kSharedSmallDownRows (down) and 256-row tiles beyond; a single segment too
+// small to give one tile per CU has its contraction split over several tiles
+// (tile_ksplit), so that it does not re-read its weights once per 64 rows.  A streamed segment of more than 32 rows keeps three or four row
 // subtiles of activations in registers and so few weight steps in flight; the
 // 64-row tiles stage both operands in LDS instead.  The limits are measured
 // choices on MI355X.
@@ -100,7 +99,7 @@ constexpr int kStreamMaxRows = 32;
 constexpr int kSharedStreamMaxRows = 32;
 constexpr int kSmallTileMaxRows = 128;
 constexpr int kSharedSmallGateUpRows = 128;
-constexpr int kSharedSmallDownRows = 512;
+constexpr int kSharedSmallDownRows = 128;
 struct TileSeg {
   const void* x = nullptr;         // activation rows (x, or H for the down projection)
   int x_rows = 0;
@@ -116,7 +115,7 @@ struct TileSeg {
   const void* w1 = nullptr;        // row-major: up (gate/up)
   const void* packed = nullptr;    // packed part (expert-strided), or nullptr
   void* out = nullptr;             // H (gate/up) or y (down)
-  // Contraction split (64-row tiles only): with ksplit > 1 each tile computes
+  // Contraction split: with ksplit > 1 each tile computes
   // 1/ksplit of the contraction and writes float32 partial sums to `part` instead
   // of `out`: [ksplit][rows][d] for down; for gate/up the gate sums
   // [ksplit][rows][inter] followed by the up sums in the same shape.
@@ -137,11 +136,11 @@ bool tile_path_ok(int d, int inter);
 hipError_t launch_ffn_tile_w8(bool gateup, int d, const TileSeg& a, const TileSeg* b,
                               hipStream_t st);
 bool tile_path_w8_ok(int d, int inter);
-// Contraction slices for a single segment of `rows` rows on the 64-row tiles with
-// contraction K and `col_tiles` weight tiles per row tile: enough tiles to cover
-// the CUs (planned for 256 of them), at least 12 stages of 64 per slice.  1 = no
-// split.  Depends on the sizes only.
-int tile_ksplit(int rows, int K, int col_tiles);
+// Contraction slices for a single segment of `rows` rows on tiles of `tile_rows`
+// rows with contraction K and `col_tiles` weight tiles per row tile: as many as
+// still fit one round of workgroups (planned for 256 CUs), at least 12 stages of
+// 64 per slice.  1 = no split.  Depends on the sizes only.
+int tile_ksplit(int rows, int K, int col_tiles, int tile_rows = 64);
 // H = silu(sum of gate partials) * (sum of up partials), slices added in order, bf16
 hipError_t launch_swiglu_parts(const float* part, int ksplit, int rows, int inter, void* h,
                                hipStream_t st);

@@ -203,7 +203,10 @@ template <int kM> __device__ __forceinline__ int seg_total_tiles(const TileSeg& 
   return s;
 }
 
-template <bool GATEUP, bool BIG, bool W8>
+// SPLIT (big shape only): every tile computes one slice of the contraction and
+// writes float32 partial sums (a separate instantiation, so that the plain big
+// kernels keep their registers).  The small shape handles both at run time.
+template <bool GATEUP, bool BIG, bool W8, bool SPLIT = false>
 __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
   typedef bf16 E;
   typedef TileShape<GATEUP, BIG, W8> S;
@@ -219,8 +222,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   const int w = tid >> 6, l = tid & 63;
   // ---- the tile lists (every wave computes the totals) -----------------------
   // entries per row tile: weight tiles times contraction slices (slice-major)
-  const int nta = (GATEUP ? a.inter / S::kFeat : d / S::kWRows) * (BIG ? 1 : a.ksplit);
-  const int ntb = b.n_exp ? (GATEUP ? b.inter / S::kFeat : d / S::kWRows) * (BIG ? 1 : b.ksplit) : 0;
+  constexpr bool kSliced = !BIG || SPLIT;   // this instantiation handles slices
+  const int nta = (GATEUP ? a.inter / S::kFeat : d / S::kWRows) * (kSliced ? a.ksplit : 1);
+  const int ntb = b.n_exp ? (GATEUP ? b.inter / S::kFeat : d / S::kWRows) * (kSliced ? b.ksplit : 1) : 0;
   const int ma = seg_total_tiles<S::kM>(a);
   const int mb = b.n_exp ? seg_total_tiles<S::kM>(b) : 0;
   // every XCD takes an equal share of each segment; the segment with the longer
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       seg = (which == 0) == b_first ? 1 : 0;
       const TileSeg& g = seg ? b : a;
       const int ntg = seg ? ntb : nta;
-      const int ntc = ntg / (BIG ? 1 : g.ksplit);  // weight tiles per row tile
+      const int ntc = ntg / (kSliced ? g.ksplit : 1);  // weight tiles per row tile
       nt = t % ntg;
       ks = nt / ntc;
       nt -= ks * ntc;
@@ -270,10 +274,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   const int e = s_tile[1];
   const int row0 = s_tile[2], rows = s_tile[3];
   const int nt = s_tile[4];
-  // contraction slices exist for the small shape only
-  const int kslice = BIG ? 0 : s_tile[5];
+  const int kslice = kSliced ? s_tile[5] : 0;
   const int K = GATEUP ? d : g.inter;              // contraction length of this segment
-  const int nk = K / kTileK / (BIG ? 1 : g.ksplit);  // stages of this tile's slice
+  const int nk = K / kTileK / (kSliced ? g.ksplit : 1);  // stages of this tile's slice
   const int kb0 = kslice * nk;                     // its first stage
 
   // LDS byte address of the buffers; the wave index as a scalar (every load below
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       }
     }
   }
-  if (!BIG && g.ksplit > 1) {
+  if (SPLIT || (!BIG && g.ksplit > 1)) {
     // float32 partial sums straight from the accumulators: register group gq of
     // block q is 4 consecutive columns (down) or features (gate/up: registers
     // 4 gq .. +3 gate, 4 gq + 8 .. +11 up) of tile row 32 (kTP wm + p) + l % 32
@@ -546,7 +549,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
         }
       }
     }
-  } else {
+  } else if constexpr (!SPLIT) {
   E* out = static_cast<E*>(g.out);
   constexpr int kNC = kOutCols * (int)sizeof(E) / 16;        // 16-byte chunks per row
   constexpr int kNCp = kNC <= 8 ? 8 : kNC <= 16 ? 16 : 32;   // ... rounded up to 2^k
@@ -617,13 +620,13 @@ static long long tile_bound(const TileSeg& g, int kM) {
   return bound;
 }
 
-template <bool GATEUP, bool BIG, bool W8 = false>
+template <bool GATEUP, bool BIG, bool W8 = false, bool SPLIT = false>
 static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStream_t st) {
   typedef TileShape<GATEUP, BIG, W8> S;
   const TileSeg bb = b ? *b : TileSeg{};
   const long long wa = GATEUP ? S::kFeat : S::kWRows;
-  const long long nta = (GATEUP ? a.inter / wa : d / wa) * a.ksplit;
-  const long long ntb = b ? (GATEUP ? bb.inter / wa : d / wa) * bb.ksplit : 0;
+  const long long nta = (GATEUP ? a.inter / wa : d / wa) * ((!BIG || SPLIT) ? a.ksplit : 1);
+  const long long ntb = b ? (GATEUP ? bb.inter / wa : d / wa) * ((!BIG || SPLIT) ? bb.ksplit : 1) : 0;
   // each segment's tiles are spread over the XCDs separately
   const long long ba = tile_bound(a, S::kM) * nta, bbn = tile_bound(bb, S::kM) * ntb;
   long long per_xcd = (ba + kXcds - 1) / kXcds + (bbn + kXcds - 1) / kXcds;
@@ -637,15 +640,15 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
   }
   const long long grid = per_xcd * kXcds;
   if (grid > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8>), dim3((unsigned)grid), dim3(kTileThreads), 0, st,
-                     a, bb, d);
+  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8, SPLIT>), dim3((unsigned)grid), dim3(kTileThreads),
+                     0, st, a, bb, d);
   return hipGetLastError();
 }
 
-int tile_ksplit(int rows, int K, int col_tiles) {
+int tile_ksplit(int rows, int K, int col_tiles, int tile_rows) {
   constexpr int kPlanCUs = 256;   // MI355X; the split depends on the sizes only
   const int nk = K / kTileK;
-  const long long tiles = (long long)((rows + 63) / 64) * col_tiles;
+  const long long tiles = (long long)((rows + tile_rows - 1) / tile_rows) * col_tiles;
   int best = 1;   // the most slices that still fit one round of workgroups
   for (int ks = 2; ks <= 8; ++ks)
     if (nk % ks == 0 && nk / ks >= 12 && tiles * ks <= kPlanCUs) best = ks;
@@ -654,8 +657,13 @@ int tile_ksplit(int rows, int K, int col_tiles) {
 
 hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const TileSeg* b,
                            hipStream_t st) {
-  // contraction slices are a 64-row-tile feature
-  if (big && (a.ksplit > 1 || (b && b->ksplit > 1))) return hipErrorInvalidValue;
+  // big tiles with contraction slices: a launch of sliced segments only
+  const bool sliced = a.ksplit > 1 || (b && b->ksplit > 1);
+  if (big && sliced) {
+    if ((a.n_exp && a.ksplit == 1) || (b && b->n_exp && b->ksplit == 1)) return hipErrorInvalidValue;
+    return gateup ? launch_shape<true, true, false, true>(d, a, b, st)
+                  : launch_shape<false, true, false, true>(d, a, b, st);
+  }
   if (gateup) return big ? launch_shape<true, true>(d, a, b, st) : launch_shape<true, false>(d, a, b, st);
   return big ? launch_shape<false, true>(d, a, b, st) : launch_shape<false, false>(d, a, b, st);
 }

@@ -402,7 +402,7 @@ def test_layer_one_expert_per_group_takes_everything(lib, name, T):
 
 
 @pytest.mark.parametrize("name,T,split_shared", [("C0", 64, False), ("C1", 64, True),
-                                                 ("C1", 17, False), ("C2", 456, False)])
+                                                 ("C1", 17, False), ("C2", 456, True)])
 def test_layer_deterministic_and_equal_to_step_path(lib, name, T, split_shared):
     import torch
     cfg = CONFIGS[name]
