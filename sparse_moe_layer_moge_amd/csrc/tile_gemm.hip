@@ -153,11 +153,13 @@ __device__ __forceinline__ int seg_expert_tiles(const TileSeg& g, int e, int* lo
   return (c > g.thr && c <= g.thr_hi) ? (c + kM - 1) / kM : 0;
 }
 
-// Find the row tile `mt` of a segment: expert, first row, rows.  Every lane of the
-// wave takes part (the prefix over experts is a wave scan).
+// Find the expert that owns row tile `mt` of a segment (row tiles numbered expert
+// by expert): the expert, its first row and row count, the index of its first row
+// tile and its number of row tiles.  Every lane of the wave takes part (the prefix
+// over experts is a wave scan).
 template <int kM>
-__device__ __forceinline__ bool seg_find_tile(const TileSeg& g, int mt, int* e_out, int* row0,
-                                              int* rows) {
+__device__ __forceinline__ bool seg_find_expert(const TileSeg& g, int mt, int* e_out, int* lo_out,
+                                                int* cnt_out, int* first_out, int* nrt_out) {
   const int l = threadIdx.x & 63;
   int base = 0;
   for (int e0 = 0; e0 < g.n_exp; e0 += 64) {
@@ -176,14 +178,11 @@ __device__ __forceinline__ bool seg_find_tile(const TileSeg& g, int mt, int* e_o
     const uint64_t m = __ballot(mine);
     if (m) {
       const int src = __ffsll((long long)m) - 1;
-      const int e_hit = __shfl(e, src, 64);
-      const int s_hit = __shfl(start, src, 64);
-      const int lo_hit = __shfl(lo, src, 64);
-      const int c_hit = __shfl(cnt, src, 64);
-      const int j = mt - s_hit;
-      *e_out = e_hit;
-      *row0 = lo_hit + j * kM;
-      *rows = min(kM, c_hit - j * kM);
+      *e_out = __shfl(e, src, 64);
+      *first_out = __shfl(start, src, 64);
+      *lo_out = __shfl(lo, src, 64);
+      *cnt_out = __shfl(cnt, src, 64);
+      *nrt_out = __shfl(nt, src, 64);
       return true;
     }
     base += __shfl(inc, 63, 64);
@@ -253,10 +252,22 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       const TileSeg& g = seg ? b : a;
       const int ntg = seg ? ntb : nta;
       const int ntc = ntg / (kSliced ? g.ksplit : 1);  // weight tiles per row tile
-      nt = t % ntg;
-      ks = nt / ntc;
-      nt -= ks * ntc;
-      if (!seg_find_tile<S::kM>(g, t / ntg, &e, &row0, &rows) || rows <= 0) seg = -1;
+      // An expert with R row tiles owns entries [ntg * first, ntg * (first + R)),
+      // row tile fastest: its R row tiles of one weight tile are neighbouring
+      // entries, which run at the same time on the same XCD and share its L2.
+      int lo = 0, cnt = 0, first = 0, nrt = 1;
+      if (seg_find_expert<S::kM>(g, t / ntg, &e, &lo, &cnt, &first, &nrt)) {
+        const int j = t - ntg * first;
+        const int mt = j % nrt;
+        nt = j / nrt;
+        ks = nt / ntc;
+        nt -= ks * ntc;
+        row0 = lo + mt * S::kM;
+        rows = min(S::kM, cnt - mt * S::kM);
+        if (rows <= 0) seg = -1;
+      } else {
+        seg = -1;
+      }
     }
     if (l == 0) {
       s_tile[0] = seg;
