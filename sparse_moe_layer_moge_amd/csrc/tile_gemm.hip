@@ -28,7 +28,8 @@
 // The loads of later stages are spread between the MFMAs of the current one; a
 // stage boundary is a wait for the wave's own loads plus a workgroup barrier.  The
 // big tile keeps 2 activation and 3 weight stages in LDS; the small tile keeps 6 of
-// both, enough bytes in flight to cover HBM latency with one workgroup per CU.
+// both, enough bytes in flight to cover HBM latency with one workgroup per CU (on
+// int8 codes 4 of both, two workgroups per CU).
 //
 // The tiles of a segment form one list: for every expert in the shape's row range
 // ceil(rows / tile rows) row tiles, each paired with every weight tile.  The list
@@ -53,6 +54,11 @@ constexpr int kTileThreads = 256;       // 4 waves
 constexpr int kXcds = 8;
 constexpr int kRowsPerLoad = 8;         // A rows one wave instruction moves
 constexpr int kFragBytes = 1024;        // one 16 x 32 bf16 MFMA fragment
+// The small shape on int8 codes: half-size weight stages, so two workgroups share
+// a CU, each with 4-deep rings (one workgroup's tile changes, pipeline fills and
+// epilogues overlap the other's loads; 2 x 4 and 3 x 3 measured alike, 1 x 6 slower)
+constexpr int kSmallW8PerCU = 2;
+constexpr int kSmallW8Depth = 4;
 
 // W8: int8 weight codes (w8_layout.hpp) instead of bf16 weights, small shape only.
 template <bool GATEUP, bool BIG, bool W8 = false> struct TileShape {
@@ -64,8 +70,9 @@ template <bool GATEUP, bool BIG, bool W8 = false> struct TileShape {
   static constexpr int kTP = kM / kWavesM / 32;                    // 32-row blocks per wave
   static constexpr int kBlocksPerTile = kWRows / 32;               // 32-row weight blocks
   static constexpr int kWP = kBlocksPerTile / kWavesN;             // ... per wave
-  static constexpr int kDA = BIG ? 2 : 6;                          // activation stages in LDS
-  static constexpr int kDB = BIG ? 3 : 6;                          // weight stages in LDS
+  static constexpr int kPerCU = W8 ? kSmallW8PerCU : 1;            // workgroups per CU
+  static constexpr int kDA = BIG ? 2 : (W8 ? kSmallW8Depth : 6);   // activation stages in LDS
+  static constexpr int kDB = BIG ? 3 : (W8 ? kSmallW8Depth : 6);   // weight stages in LDS
   static constexpr int kAStageBytes = kM * kLineBytes;
   // B stage: bf16 weights, kWRows / 8 fragments of 1 KiB; int8 codes, kWRows / 16
   // code tiles of 1 KiB (16 rows x 64 codes)
@@ -78,7 +85,7 @@ template <bool GATEUP, bool BIG, bool W8 = false> struct TileShape {
   static constexpr int kEvery = BIG ? (GATEUP ? 2 : 3) : 1;
   static_assert(kDA <= kDB && (kDA == kDB || (kDA == 2 && kDB == 3)), "ring depths");
   static_assert(kWP * kWavesN == kBlocksPerTile && kTP >= 1, "wave layout");
-  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(kLdsBytes * kPerCU <= 160 * 1024, "LDS budget");
   static_assert((kALoads + kBLoads) * kEvery <= 4 * kTP * kWP, "loads must fit in a stage");
   static_assert(!(W8 && BIG), "int8 codes use the small shape");
 };
@@ -233,7 +240,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   const int tot0 = b_first ? mb * ntb : ma * nta, tot1 = b_first ? ma * nta : mb * ntb;
   const int ch0 = (tot0 + kXcds - 1) / kXcds, ch1 = (tot1 + kXcds - 1) / kXcds;
   // workgroup b runs on XCD b % 8 and takes that XCD's entry b / 8; the small shape
-  // (launched with at most one workgroup per CU) walks on to b / 8 + G, b / 8 + 2G,
+  // (launched with as many workgroups as fit the CUs) walks on to b / 8 + G, b / 8 + 2G,
   // ... (G workgroups per XCD), so the CUs of an XCD work on neighbouring entries
   const int x = blockIdx.x % kXcds;
   auto run_tile = [&](int it) {
@@ -643,10 +650,10 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
   long long per_xcd = (ba + kXcds - 1) / kXcds + (bbn + kXcds - 1) / kXcds;
   if (per_xcd == 0) return hipSuccess;
   if (!BIG) {
-    // at most one workgroup per CU (the LDS rings take most of a CU's LDS), each
-    // walking its XCD's share of the list: the bound counts every expert that
-    // could fall in the range, and a launch that finds none stays cheap
-    const long long slots = device_cus() / kXcds;
+    // as many workgroups as fit the CUs at once (the LDS rings take most of a CU's
+    // LDS), each walking its XCD's share of the list: the bound counts every
+    // expert that could fall in the range, and a launch that finds none stays cheap
+    const long long slots = device_cus() * S::kPerCU / kXcds;
     if (per_xcd > slots) per_xcd = slots > 0 ? slots : 1;
   }
   const long long grid = per_xcd * kXcds;
