@@ -126,6 +126,10 @@ struct TileSeg {
   // [n_exp, d]) and sc1 those of the up rows
   const float* sc0 = nullptr;
   const float* sc1 = nullptr;
+  // 64-row bf16 tiles: mark the weight loads non-temporal (weights of experts
+  // with few rows each, read once per launch, so that they do not push the
+  // activation rows every weight tile re-reads out of L2)
+  bool nt_weights = false;
 };
 // big: 256-row tiles; otherwise 64-row tiles
 hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const TileSeg* b,

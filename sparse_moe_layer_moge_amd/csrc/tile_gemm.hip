@@ -117,6 +117,13 @@ __device__ __forceinline__ void lds_dma16(Rsrc r, uint32_t voff, uint32_t soff, 
                : "memory");
 }
 
+// the same, marked non-temporal (data read once)
+__device__ __forceinline__ void lds_dma16_nt(Rsrc r, uint32_t voff, uint32_t soff, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(r), "s"(soff)
+               : "memory");
+}
 // wait until at most N of this wave's vector-memory operations are outstanding
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N < 64, "vmcnt field is 6 bits");
@@ -377,9 +384,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
     const uint32_t st = ldsA0 + (uint32_t)((s % S::kDA) * S::kAStageBytes);
     lds_dma16(xr, a_voff[i], s * a_step, st + (wu * S::kALoads + i) * kRowsPerLoad * kLineBytes);
   };
+  // non-temporal weight loads: bf16 64-row tiles of a segment that asks for them
+  const bool b_nt = !BIG && !W8 && g.nt_weights;
   auto issue_b = [&](int i, int s) {
     const uint32_t st = ldsB0 + (uint32_t)((s % S::kDB) * S::kBStageBytes);
-    lds_dma16(b_rsrc(i), b_voff[i], s * b_step, st + (wu * S::kBLoads + i) * kFragBytes);
+    if (b_nt)
+      lds_dma16_nt(b_rsrc(i), b_voff[i], s * b_step, st + (wu * S::kBLoads + i) * kFragBytes);
+    else
+      lds_dma16(b_rsrc(i), b_voff[i], s * b_step, st + (wu * S::kBLoads + i) * kFragBytes);
   };
 
   // ---- wave tile: kTP 32-row blocks x kWP 32-weight-row blocks.
