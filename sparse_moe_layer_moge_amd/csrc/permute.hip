@@ -21,12 +21,13 @@ namespace moge {
 constexpr int kSmallWaves = 16;  // waves of the single-workgroup kernel
 constexpr int kSmallChunks = 8;  // chunks up to which it is used (T <= 512): beyond
                                  // that the chunk-parallel kernels finish sooner
+constexpr int kSmallIdxCache = 4096;  // slot indices (T * K) it stages in LDS
 
 // f(k, e) for every slot k of token t, in slot order.  The slot indices are
 // loaded 8 at a time before any is used, so a token's loads overlap instead of
 // paying one memory latency each.
 template <typename F>
-__device__ __forceinline__ void for_each_slot(const int32_t* __restrict__ idx, int t, int K, F&& f) {
+__device__ __forceinline__ void for_each_slot(const int32_t* idx, int t, int K, F&& f) {
   const int32_t* p = idx + (size_t)t * K;
   for (int k0 = 0; k0 < K; k0 += 8) {
     int e[8];
@@ -40,7 +41,7 @@ __device__ __forceinline__ void for_each_slot(const int32_t* __restrict__ idx, i
 
 // The set of experts token t chose (entries outside [0, N) and repeats ignored;
 // moge_route never produces either).
-__device__ __forceinline__ void chosen_set(const int32_t* __restrict__ idx, int t, int K, int N,
+__device__ __forceinline__ void chosen_set(const int32_t* idx, int t, int K, int N,
                                            bool valid, uint64_t (&chosen)[4]) {
   chosen[0] = chosen[1] = chosen[2] = chosen[3] = 0ull;
   if (!valid) return;
@@ -135,18 +136,28 @@ __device__ __forceinline__ void expert_offsets(const int32_t* cnt, int N, int32_
 // ---------------------------------------------------------------------------
 // single workgroup: T <= 64 * kSmallChunks.  The masks and counts are split by
 // (chunk, slice of the experts) and the scatter by (chunk, slot), so that a
-// decode batch of one chunk still spreads over every wave.
+// decode batch of one chunk still spreads over every wave.  kCached: the slot
+// indices (T * K <= kSmallIdxCache) are copied to LDS first, so that the scatter's
+// reads of them (several units per wave, each a dependent read) cost LDS latency.
 // ---------------------------------------------------------------------------
+template <bool kCached>
 __global__ __launch_bounds__(64 * kSmallWaves) void k_permute_small(
-    const int32_t* __restrict__ idx, int T, int K, int N, int M, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ idx_g, int T, int K, int N, int M, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ group_counts,
     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row) {
   __shared__ uint64_t s_mask[kSmallChunks][256];  // tokens of chunk c that chose e
   __shared__ int32_t s_base[kSmallChunks][256];   // those tokens in chunks before c
   __shared__ int32_t s_cnt[256];
   __shared__ int32_t s_off[257];
+  __shared__ int32_t s_idx[kCached ? kSmallIdxCache : 1];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int nchunks = (T + 63) / 64;
+  const int32_t* idx = idx_g;
+  if constexpr (kCached) {
+    for (int i = threadIdx.x; i < T * K; i += blockDim.x) s_idx[i] = idx_g[i];
+    __syncthreads();
+    idx = s_idx;
+  }
 
   // masks and per-chunk counts: wave w takes chunk w % nchunks and every S-th
   // expert from w / nchunks on (S waves per chunk)
@@ -285,8 +296,12 @@ hipError_t launch_permute(const int32_t* idx, int T, int K, int N, int M, int32_
                           hipStream_t st) {
   const int nblk = perm_blocks(T);
   if (nblk <= kSmallChunks) {
-    hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(64 * kSmallWaves), 0, st, idx, T, K, N, M,
-                       counts, offsets, group_counts, sorted_pair, pair_row);
+    if ((long long)T * K <= kSmallIdxCache)
+      hipLaunchKernelGGL(k_permute_small<true>, dim3(1), dim3(64 * kSmallWaves), 0, st, idx, T, K,
+                         N, M, counts, offsets, group_counts, sorted_pair, pair_row);
+    else
+      hipLaunchKernelGGL(k_permute_small<false>, dim3(1), dim3(64 * kSmallWaves), 0, st, idx, T,
+                         K, N, M, counts, offsets, group_counts, sorted_pair, pair_row);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_chunk_hist, dim3(nblk), dim3(64), 0, st, idx, T, K, N, blk_cnt);
