@@ -182,6 +182,9 @@ static bool router_tiles(int dtype, int T, int d) {
   return dtype == 1 && T >= kRtMinTokens && d % 64 == 0;
 }
 
+// contraction splits of the router scores (k_route sums at most this many)
+constexpr int kMaxRouterSplit = 16;
+
 int router_ksplit(int dtype, int T, int d, int N) {
   if (router_tiles(dtype, T, d)) {
     // about one workgroup per CU, with no empty split
@@ -189,7 +192,7 @@ int router_ksplit(int dtype, int T, int d, int N) {
     const int nst = d / 64;
     int ks = 256 / (tiles > 0 ? tiles : 1);
     if (ks < 1) ks = 1;
-    if (ks > 16) ks = 16;
+    if (ks > kMaxRouterSplit) ks = kMaxRouterSplit;
     if (ks > nst) ks = nst;
     const int per = (nst + ks - 1) / ks;
     return (nst + per - 1) / per;
@@ -200,7 +203,7 @@ int router_ksplit(int dtype, int T, int d, int N) {
   const int nsteps = d / 32;
   int ks = 512 / (tiles > 0 ? tiles : 1);
   if (ks < 1) ks = 1;
-  if (ks > 16) ks = 16;
+  if (ks > kMaxRouterSplit) ks = kMaxRouterSplit;
   if (ks > nsteps) ks = nsteps;
   return ks;
 }
@@ -256,12 +259,19 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ partial
     const int e = l + 64 * j;
     v[j] = -INFINITY;
     if (e < N) {
-      // start from split 0 (not from 0.f) so a lone -0.0 score keeps its sign;
-      // splits are added in increasing order (loads batched by the unroll)
-      float s = partial[(size_t)tt * N + e];
-#pragma unroll 8
-      for (int ks = 1; ks < ksplit; ++ks) s += partial[((size_t)ks * T + tt) * N + e];
-      if (bias) s += bias[e];
+      // every split's partial is loaded before any is added (one memory latency,
+      // not one per batch); start from split 0 (not from 0.f) so a lone -0.0
+      // score keeps its sign, and add the splits in increasing order
+      float pv[kMaxRouterSplit];
+#pragma unroll
+      for (int ks = 0; ks < kMaxRouterSplit; ++ks)
+        pv[ks] = ks < ksplit ? partial[((size_t)ks * T + tt) * N + e] : 0.f;
+      const float b = bias ? bias[e] : 0.f;
+      float s = pv[0];
+#pragma unroll
+      for (int ks = 1; ks < kMaxRouterSplit; ++ks)
+        if (ks < ksplit) s += pv[ks];
+      if (bias) s += b;
       v[j] = s;
       mx = fmaxf(mx, s);
     }
@@ -313,6 +323,7 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ partial
 hipError_t launch_route(const float* partial, int ksplit, int T, int N, int M, int kp,
                         const float* bias, float* logits_out, float* probs, int32_t* idx,
                         float* gate, hipStream_t st) {
+  if (ksplit < 1 || ksplit > kMaxRouterSplit) return hipErrorInvalidValue;
   dim3 grid((T + kRouteWaves - 1) / kRouteWaves);
   hipLaunchKernelGGL(k_route, grid, dim3(64 * kRouteWaves), 0, st, partial, ksplit, T, N, M, kp,
                      bias, logits_out, probs, idx, gate);
