@@ -39,9 +39,11 @@ template <> struct Vec8Io<float> {
   }
 };
 
-// grid (T, ceil(d / 512)); thread = 8 consecutive features of one token.  The
-// slot loop is unrolled by 8 so the K row loads of a token are in flight together;
-// the additions still run in slot order.
+// grid (T, ceil(d / 512)); thread = 8 consecutive features of one token.  Loads go
+// out in batches so that a thread waits for memory about twice, not once per
+// term: the first 8 slots' rows and gates together with every partial slice of
+// the shared term, then those slots' y_perm rows (with the next 8 slots' rows
+// and gates).  The additions still run in slice order, then slot order.
 template <typename E>
 __global__ __launch_bounds__(64) void k_combine(int T, int K, int d, int R,
                                                 const E* __restrict__ y_perm,
@@ -53,15 +55,36 @@ __global__ __launch_bounds__(64) void k_combine(int T, int K, int d, int R,
   const int t = blockIdx.x;
   const int c = blockIdx.y * 64 + threadIdx.x;
   if (c >= d / 8) return;
+  int rows[8];
+  float g[8];
+  // (slots past K read slot K - 1 and are dropped: no branch per load, so the
+  // 16 scalar loads go out together)
+  auto load_slots = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = min(k0 + j, K - 1);
+      rows[j] = pair_row[(size_t)t * K + k];
+      g[j] = gate[(size_t)t * K + k];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j >= K) rows[j] = -1;
+  };
+  load_slots(0);
   float acc[8];
   if (shared_part) {
-    Vec8Io<float>::load(shared_part + (size_t)t * d + c * 8, acc);
-    for (int p = 1; p < n_part; ++p) {
-      float v[8];
-      Vec8Io<float>::load(shared_part + ((size_t)p * T + t) * d + c * 8, v);
+    float sp[kMaxSlices][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    }
+    for (int p = 0; p < kMaxSlices; ++p)
+      if (p < n_part) Vec8Io<float>::load(shared_part + ((size_t)p * T + t) * d + c * 8, sp[p]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = sp[0][i];
+#pragma unroll
+    for (int p = 1; p < kMaxSlices; ++p)
+      if (p < n_part) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += sp[p][i];
+      }
   } else if (shared) {
     Vec8Io<E>::load(shared + (size_t)t * d + c * 8, acc);
   } else {
@@ -69,14 +92,7 @@ __global__ __launch_bounds__(64) void k_combine(int T, int K, int d, int R,
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   }
   for (int k0 = 0; k0 < K; k0 += 8) {
-    int rows[8];
-    float g[8], v[8][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = k0 + j;
-      rows[j] = k < K ? pair_row[(size_t)t * K + k] : -1;
-      g[j] = k < K ? gate[(size_t)t * K + k] : 0.f;
-    }
+    float v[8][8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (rows[j] >= 0 && rows[j] < R) {
@@ -86,11 +102,19 @@ __global__ __launch_bounds__(64) void k_combine(int T, int K, int d, int R,
         for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
       }
     }
+    int rr[8];
+    float gg[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      rr[j] = rows[j];
+      gg[j] = g[j];
+    }
+    if (k0 + 8 < K) load_slots(k0 + 8);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (k0 + j < K && rows[j] >= 0 && rows[j] < R) {
+      if (k0 + j < K && rr[j] >= 0 && rr[j] < R) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], v[j][i], acc[i]);
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(gg[j], v[j][i], acc[i]);
       }
   }
   Vec8Io<E>::store(y + (size_t)t * d + c * 8, acc);
@@ -100,6 +124,7 @@ hipError_t launch_combine(int dtype, int T, int K, int d, const void* y_perm,
                           const int32_t* pair_row, const float* gate, const void* shared,
                           const float* shared_part, int n_part, void* y, hipStream_t st) {
   if (T == 0) return hipSuccess;
+  if (shared_part && (n_part < 1 || n_part > kMaxSlices)) return hipErrorInvalidValue;
   const int R = T * K;
   dim3 grid(T, (d / 8 + 63) / 64);
   if (dtype == 1)
@@ -120,19 +145,29 @@ __global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ 
   if (i >= n8) return;
   const size_t plane = (size_t)rows * inter;
   const float* up = part + (size_t)ksplit * plane;
-  float g[8], u[8];
-  Vec8Io<float>::load(part + i * 8, g);
-  Vec8Io<float>::load(up + i * 8, u);
-  for (int s = 1; s < ksplit; ++s) {
-    float a[8], b[8];
-    Vec8Io<float>::load(part + s * plane + i * 8, a);
-    Vec8Io<float>::load(up + s * plane + i * 8, b);
+  // every slice's loads go out before any is added
+  float a[kMaxSlices][8], b[kMaxSlices][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      g[j] += a[j];
-      u[j] += b[j];
+  for (int s = 0; s < kMaxSlices; ++s)
+    if (s < ksplit) {
+      Vec8Io<float>::load(part + s * plane + i * 8, a[s]);
+      Vec8Io<float>::load(up + s * plane + i * 8, b[s]);
     }
+  float g[8], u[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    g[j] = a[0][j];
+    u[j] = b[0][j];
   }
+#pragma unroll
+  for (int s = 1; s < kMaxSlices; ++s)
+    if (s < ksplit) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        g[j] += a[s][j];
+        u[j] += b[s][j];
+      }
+    }
   float v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = silu(g[j]) * u[j];
@@ -143,6 +178,7 @@ hipError_t launch_swiglu_parts(const float* part, int ksplit, int rows, int inte
                                hipStream_t st) {
   const size_t n8 = (size_t)rows * inter / 8;
   if (n8 == 0) return hipSuccess;
+  if (ksplit < 1 || ksplit > kMaxSlices) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_swiglu_parts, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, part,
                      ksplit, rows, inter, (bf16*)h);
   return hipGetLastError();

@@ -143,7 +143,8 @@ bool tile_path_w8_ok(int d, int inter);
 // Contraction slices for a single segment of `rows` rows on tiles of `tile_rows`
 // rows with contraction K and `col_tiles` weight tiles per row tile: as many as
 // still fit one round of workgroups (planned for 256 CUs), at least 12 stages of
-// 64 per slice.  1 = no split.  Depends on the sizes only.
+// 64 per slice.  1 = no split, at most kMaxSlices.  Depends on the sizes only.
+constexpr int kMaxSlices = 8;
 int tile_ksplit(int rows, int K, int col_tiles, int tile_rows = 64);
 // H = silu(sum of gate partials) * (sum of up partials), slices added in order, bf16
 hipError_t launch_swiglu_parts(const float* part, int ksplit, int rows, int inter, void* h,

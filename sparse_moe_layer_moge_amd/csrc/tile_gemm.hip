@@ -680,7 +680,7 @@ int tile_ksplit(int rows, int K, int col_tiles, int tile_rows) {
   const int nk = K / kTileK;
   const long long tiles = (long long)((rows + tile_rows - 1) / tile_rows) * col_tiles;
   int best = 1;   // the most slices that still fit one round of workgroups
-  for (int ks = 2; ks <= 8; ++ks)
+  for (int ks = 2; ks <= kMaxSlices; ++ks)
     if (nk % ks == 0 && nk / ks >= 12 && tiles * ks <= kPlanCUs) best = ks;
   return best;
 }
