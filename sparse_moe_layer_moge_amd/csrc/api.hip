@@ -253,12 +253,35 @@ moge::TileSeg tile_view(const moge::FfnSeg& f, bool gateup) {
   return t;
 }
 
-// Both projections of up to two segments.  The streaming kernels take routed
-// experts with at most kStreamMaxRows rows, the 64-row tile kernels those with up
-// to kSmallTileMaxRows, the 256-row tile kernels the rest; the shared segment has
-// its own limits (kSharedStreamMaxRows, kSharedSmallGateUpRows, kSharedSmallDownRows).  A tile launch is
-// made only when some expert can fall in its range (an expert never has more rows
-// than the batch has tokens).
+// Row ranges of the routed experts: the streaming kernels take experts with at
+// most `stream_max` rows, the 64-row tiles those up to `small_max`, the 256-row
+// tiles the rest.  Each expert's kernel is chosen on the device from its row
+// count, and the host cannot see the counts, so every range gets a launch, and a
+// launch that finds no expert still costs about 4 us.  The mean rows per expert
+// (R / N) is known on the host; a range that is unlikely to hold an expert at that
+// mean joins its neighbour (any kernel handles any row count):
+//   mean >= 1.5 * kStreamMaxRows:    experts of up to kStreamMaxRows rows take the
+//                                    64-row tiles (no streaming launch);
+//   mean <= kSmallTileMaxRows / 2:   experts above kSmallTileMaxRows rows stay on
+//                                    64-row tiles (no 256-row launch);
+//   mean >= 2 * kSmallTileMaxRows:   every routed expert takes 256-row tiles.
+struct RoutedRanges {
+  int stream_max, small_max;
+};
+RoutedRanges routed_ranges(long long R, int N, bool big_tiles) {
+  RoutedRanges r{moge::kStreamMaxRows, big_tiles ? moge::kSmallTileMaxRows : INT_MAX};
+  const double mean = N > 0 ? (double)R / N : 0.0;
+  if (mean >= 1.5 * moge::kStreamMaxRows) r.stream_max = 0;
+  if (big_tiles && mean <= moge::kSmallTileMaxRows / 2) r.small_max = INT_MAX;
+  if (big_tiles && mean >= 2.0 * moge::kSmallTileMaxRows) r.stream_max = r.small_max = 0;
+  return r;
+}
+
+// Both projections of up to two segments.  The routed experts go to the streaming,
+// 64-row and 256-row kernels by the ranges routed_ranges gives; the shared segment
+// has its own limits (kSharedStreamMaxRows, kSharedSmallGateUpRows,
+// kSharedSmallDownRows).  A tile launch is made only when some expert can fall in
+// its range (an expert never has more rows than the batch has tokens).
 // split: contraction slices for the shared segment's 64-row tiles, with sh_part
 // the float32 partial-sum region (used when a slice count is above 1).
 moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh,
@@ -267,12 +290,17 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
   // the tile path covers bf16 and its tile shapes; everything else streams
   const bool tiles_ok = dtype == MOGE_BF16 && moge::tile_path_ok(d, routed.inter) &&
                         (!sh || moge::tile_path_ok(d, sh->inter));
-  const int thr = tiles_ok ? moge::kStreamMaxRows : INT_MAX;
+  const RoutedRanges rr = routed_ranges(routed.rows, routed.n_exp, true);
+  const int thr = tiles_ok ? rr.stream_max : INT_MAX;
   const int sh_thr = tiles_ok ? moge::kSharedStreamMaxRows : INT_MAX;
-  const int thr_big = moge::kSmallTileMaxRows;
+  const int thr_big = rr.small_max;
   routed.thr = thr;
   if (sh) sh->thr = sh_thr;
   const bool sh_stream = sh && sh->rows <= sh_thr;
+  // the streaming launches, with the routed experts only when their range is open
+  moge::FfnSeg rs = routed;
+  if (thr == 0) rs.n_exp = 0;
+  const bool stream_launch = rs.n_exp > 0 || sh_stream;
   // tile launches: routed experts with lo < rows <= hi, the shared segment with
   // sh_lo < rows <= sh_hi
   struct Range { int lo, hi, sh_lo, sh_hi; bool big; };
@@ -280,14 +308,14 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
     const int sh_big = gateup ? moge::kSharedSmallGateUpRows : moge::kSharedSmallDownRows;
     const Range ranges[2] = {{thr, thr_big, sh_thr, sh_big, false},
                              {thr_big, INT_MAX, sh_big, INT_MAX, true}};
-    if (gateup)
-      CHECK(hip_check(moge::launch_ffn_gateup(dtype, d, routed, sh_stream ? sh : nullptr, st),
+    if (stream_launch && gateup)
+      CHECK(hip_check(moge::launch_ffn_gateup(dtype, d, rs, sh_stream ? sh : nullptr, st),
                       "expert gate/up"));
-    else
-      CHECK(hip_check(moge::launch_ffn_down(dtype, d, routed, sh_stream ? sh : nullptr, st),
+    else if (stream_launch)
+      CHECK(hip_check(moge::launch_ffn_down(dtype, d, rs, sh_stream ? sh : nullptr, st),
                       "expert down"));
     for (const Range& rg : ranges) {
-      const bool routed_here = tiles_ok && T > rg.lo;
+      const bool routed_here = tiles_ok && T > rg.lo && rg.lo < rg.hi;
       const bool sh_here = tiles_ok && sh && sh->rows > rg.sh_lo && sh->rows <= rg.sh_hi;
       if (!routed_here && !sh_here) continue;
       moge::TileSeg a = tile_view(routed, gateup);
@@ -342,15 +370,18 @@ moge_status_t run_ffn_w8(int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh, h
                          bool marks, SharedSplit split, float* sh_part) {
   const bool tiles = moge::tile_path_w8_ok(d, routed.inter) &&
                      (!sh || moge::tile_path_w8_ok(d, sh->inter));
-  routed.thr = tiles ? moge::kStreamMaxRows : INT_MAX;
+  routed.thr = tiles ? routed_ranges(routed.rows, routed.n_exp, false).stream_max : INT_MAX;
   if (sh) sh->thr = tiles ? moge::kSharedStreamMaxRows : INT_MAX;
   const bool sh_stream = sh && sh->rows <= sh->thr;
+  moge::FfnSeg rs = routed;
+  if (routed.thr == 0) rs.n_exp = 0;
+  const bool stream_launch = rs.n_exp > 0 || sh_stream;
   for (int gateup = 1; gateup >= 0; --gateup) {
-    if (gateup)
-      CHECK(hip_check(moge::launch_ffn_gateup_w8(d, routed, sh_stream ? sh : nullptr, st),
+    if (stream_launch && gateup)
+      CHECK(hip_check(moge::launch_ffn_gateup_w8(d, rs, sh_stream ? sh : nullptr, st),
                       "int8 expert gate/up"));
-    else
-      CHECK(hip_check(moge::launch_ffn_down_w8(d, routed, sh_stream ? sh : nullptr, st),
+    else if (stream_launch)
+      CHECK(hip_check(moge::launch_ffn_down_w8(d, rs, sh_stream ? sh : nullptr, st),
                       "int8 expert down"));
     const bool routed_here = tiles && T > routed.thr;
     const bool sh_here = tiles && sh && !sh_stream;

@@ -55,12 +55,45 @@ def _draw_tiles(seed):
 
 CASES = list(range(24))
 
+# Skewed batches (Zipf(1.2) router bias) at the edges of the host's row-range
+# choice, which uses only the mean rows per expert R / N:
+#   mean 50 (T=400, N=64, K=8): no streaming launch, no 256-row launch, so the
+#     64-row tiles take experts of any size, from a few rows to several hundred;
+#   mean 512 (T=2048, N=16, K=4): every routed expert on 256-row tiles, the
+#     least-chosen ones with far fewer than 128 rows.
+EDGE_CASES = {
+    "mean50-skewed": replace(C0, name="mean50-skewed", T=400, d=256, N=64, M=8, kp=1, inter=192,
+                             n_shared=1, shared_inter=192, dtype="bf16", router_std=1.0 / 16,
+                             zipf_s=1.2, seed=7),
+    "mean512-skewed": replace(C0, name="mean512-skewed", T=2048, d=256, N=16, M=4, kp=1,
+                              inter=192, n_shared=1, shared_inter=192, dtype="bf16",
+                              router_std=1.0 / 16, zipf_s=1.2, seed=8),
+}
+
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("seed", CASES)
 def test_random_layer(lib, seed):
+    _check_layer(lib, _draw(seed))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name", sorted(EDGE_CASES))
+def test_row_range_edges(lib, name):
+    cfg = EDGE_CASES[name]
+    counts = np.bincount(O.route(S.make_scores(cfg, T=cfg.T), cfg.M, cfg.kp)["idx"].ravel(),
+                         minlength=cfg.N)
+    # the shapes reach what they are for
+    if name == "mean50-skewed":
+        assert counts.max() > 128 and counts.min() <= 32, counts
+    else:
+        assert counts.min() < 128, counts
+    _check_layer(lib, cfg)
+
+
+def _check_layer(lib, cfg):
     import torch
-    cfg = _draw(seed)
+    seed = cfg.seed
     T = cfg.T
     inp = S.make_layer_inputs(cfg)
     scores = S.make_scores(cfg, T=T)
