@@ -164,7 +164,7 @@ def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs the MoGE layer on one GPU only; "
+        print(json.dumps({"error": "this library runs the MoGE layer on one GPU only; "
                                    f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported. "
                                    "A multi-GPU layer would place one expert group per GPU "
                                    "(all-gather of x, reduce-scatter of the outputs)."}))
