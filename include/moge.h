@@ -128,8 +128,9 @@ moge_status_t moge_permute(const moge_dims_t* dims, const int32_t* topk_idx, con
  *   offsets [N+1] int32 in (device)   row ranges per expert, offsets[N] == R
  *   w_gate, w_up [N,I,d], w_down [N,d,I] dtype in
  *   y_perm  [R,d] dtype out
- * Each expert takes the weight-streaming path or the MFMA tile path, chosen on
- * the device from its row count. The shared experts are this call with dims
+ * Each expert takes the weight-streaming path or an MFMA tile path, chosen on the
+ * device from its row count, within row ranges the host sets from the mean rows
+ * per expert (R / N; no device data is read). The shared experts are this call with dims
  * N = M = K' = 1, inter = I_s, x_perm = x and offsets = {0, T}. */
 moge_status_t moge_expert_ffn(const moge_dims_t* dims, const void* x_perm,
                               const int32_t* offsets, const void* w_gate, const void* w_up,
