@@ -70,6 +70,22 @@ EDGE_CASES = {
                               router_std=1.0 / 16, zipf_s=1.2, seed=8),
 }
 
+# The API's limits: N = 256 experts and K = M * K' = 64 slots per token (4 groups of
+# 64, 16 from each).  T = 1 (64 experts with one row each), T = 100 (mean 25 rows:
+# streaming and 64-row tiles), T = 600 (mean 150: 64-row and 256-row tiles).
+LIMIT_CASES = [(dt, T) for dt in ("bf16", "f32") for T in (1, 100, 600)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,T", LIMIT_CASES)
+def test_layer_at_api_limits(lib, dtype, T):
+    cfg = replace(C0, name=f"limits-{dtype}-T{T}", T=T, d=256, N=256, M=4, kp=16, inter=192,
+                  n_shared=1, shared_inter=192, dtype=dtype, router_std=1.0 / 16, zipf_s=0.0,
+                  seed=11)
+    # T = 600: the oracle's float64 layer over 38400 rows takes about a minute, so
+    # its outputs are compared on 64 sampled tokens (routing on all of them)
+    _check_layer(lib, cfg, tokens=S.sample_tokens(T, 64) if T > 100 else None)
+
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("seed", CASES)
@@ -91,7 +107,7 @@ def test_row_range_edges(lib, name):
     _check_layer(lib, cfg)
 
 
-def _check_layer(lib, cfg):
+def _check_layer(lib, cfg, tokens=None):
     import torch
     seed = cfg.seed
     T = cfg.T
@@ -125,11 +141,12 @@ def _check_layer(lib, cfg):
     torch.cuda.synchronize()
     ref = O.layer(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down,
                   inp.ws_gate, inp.ws_up, inp.ws_down, M=cfg.M, kp=cfg.kp, dtype=dt,
-                  logits_f32=scores)
+                  logits_f32=scores, tokens=tokens)
+    rows = slice(None) if tokens is None else tokens
     np.testing.assert_array_equal(to_host(idx), ref["idx"])
     np.testing.assert_array_equal(to_host(idxp), ref["idx"])
     np.testing.assert_array_equal(to_host(yp), to_host(y))
-    err = normwise_rel_err(values(to_host(y)), ref["y"])
+    err = normwise_rel_err(values(to_host(y))[rows], ref["y"])
     assert err <= tolerance(cfg), err
 
     # the int8 layer where the sizes allow it (bf16, widths multiples of 64)
@@ -155,13 +172,14 @@ def _check_layer(lib, cfg):
         ref8 = O.layer_w8(inp.x, inp.w_router, inp.router_bias, q["q_gate"], q["s_gate"],
                           q["q_up"], q["s_up"], q["q_down"], q["s_down"], q["qs_gate"],
                           q["ss_gate"], q["qs_up"], q["ss_up"], q["qs_down"], q["ss_down"],
-                          M=cfg.M, kp=cfg.kp, logits_f32=scores)
+                          M=cfg.M, kp=cfg.kp, logits_f32=scores, tokens=tokens)
     else:
         # no shared experts: the int8 layer of the routed experts alone
         ref8 = O.layer(inp.x, inp.w_router, inp.router_bias, O.W8Weights(q["q_gate"], q["s_gate"]),
                        O.W8Weights(q["q_up"], q["s_up"]), O.W8Weights(q["q_down"], q["s_down"]),
                        np.zeros((0, cfg.d)), np.zeros((0, cfg.d)), np.zeros((cfg.d, 0)),
-                       M=cfg.M, kp=cfg.kp, dtype="bf16", logits_f32=scores, wdtype="f64")
+                       M=cfg.M, kp=cfg.kp, dtype="bf16", logits_f32=scores, wdtype="f64",
+                       tokens=tokens)
     np.testing.assert_array_equal(to_host(idx8), ref["idx"])
-    err8 = normwise_rel_err(values(to_host(y8)), ref8["y"])
+    err8 = normwise_rel_err(values(to_host(y8))[rows], ref8["y"])
     assert err8 <= tolerance(cfg), err8
