@@ -11,6 +11,8 @@
 // projection - and the whole contraction.  It streams those rows once per group of
 // up to 64 of the expert's token rows (stream_tile.hpp).  SwiGLU is applied to the
 // float32 accumulators before the single rounding of H.
+#include <atomic>
+
 #include <math.h>
 
 #include "moge_common.hpp"
@@ -234,16 +236,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void k_
 // ---------------------------------------------------------------------------
 // Resident wave slots of the streaming kernels (3 waves per SIMD, 4 SIMDs per CU).
 int device_cus() {
-  static int cus[64] = {0};
+  // per-device cache; concurrent first calls store the same value
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 static int stream_slots() { return 3 * 4 * device_cus(); }
