@@ -253,7 +253,7 @@ static int stream_slots() { return 3 * 4 * device_cus(); }
 
 // Blocks per wave for one segment: the divisor k <= 8 of its blocks per expert
 // whose item size (k blocks) is closest to an even share of the launch's weight
-// bytes over one round of resident waves.  Segments whose rows need more than one
+// bytes over the planned rounds of resident waves.  Segments whose rows need more than one
 // 16-row subtile run slower per byte, so they aim at half the share.
 static int blocks_per_wave(int blocks_per_expert, double block_bytes, double share,
                            int multiple) {
@@ -276,9 +276,9 @@ static int blocks_per_wave(int blocks_per_expert, double block_bytes, double sha
 static bool wide_rows(const FfnSeg& g) { return g.offsets == nullptr && g.rows > 16; }
 
 void plan_blocks(FfnSeg& a, FfnSeg* b, double a_block, double b_block, int a_bpe, int b_bpe,
-                 int multiple) {
+                 int multiple, double rounds) {
   const double total = a_block * a.n_exp * a_bpe + (b ? b_block * b->n_exp * b_bpe : 0.0);
-  const double share = total / stream_slots();
+  const double share = total / (stream_slots() * rounds);
   a.nblk = wide_rows(a) ? blocks_per_wave(a_bpe, a_block, share / 2, 1)
                         : blocks_per_wave(a_bpe, a_block, share, multiple);
   if (b)
@@ -308,7 +308,7 @@ hipError_t launch_ffn_down(int dtype, int d, const FfnSeg& a0, const FfnSeg* b0,
   FfnSeg a = a0, bb = b0 ? *b0 : FfnSeg{};
   // a block = 32 down rows over the segment's intermediate width
   plan_blocks(a, b0 ? &bb : nullptr, 32.0 * a.inter * es, b0 ? 32.0 * bb.inter * es : 0.0,
-              d / 32, b0 ? d / 32 : 0, kPairBlocks);
+              d / 32, b0 ? d / 32 : 0, kPairBlocks, kDownRounds);
   const int items_a = a.n_exp * (d / 32 / a.nblk);
   const int items_b = b0 ? bb.n_exp * (d / 32 / bb.nblk) : 0;
   if (items_a + items_b == 0) return hipSuccess;

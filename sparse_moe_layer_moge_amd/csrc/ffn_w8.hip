@@ -463,7 +463,7 @@ hipError_t launch_ffn_down_w8(int d, const FfnSeg& a0, const FfnSeg* b0, hipStre
   FfnSeg a = a0, bb = b0 ? *b0 : FfnSeg{};
   // a block = 32 down rows over the segment's intermediate width
   plan_blocks(a, b0 ? &bb : nullptr, 32.0 * a.inter, b0 ? 32.0 * bb.inter : 0.0, d / 32,
-              b0 ? d / 32 : 0, 2);
+              b0 ? d / 32 : 0, 2, kDownRounds);
   const int items_a = a.n_exp * (d / 32 / a.nblk);
   const int items_b = b0 ? bb.n_exp * (d / 32 / bb.nblk) : 0;
   if (items_a + items_b == 0) return hipSuccess;
