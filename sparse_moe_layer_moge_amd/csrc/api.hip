@@ -143,6 +143,14 @@ bool w8_tiles_ok_for(const moge_dims_t* d) {
          (d->shared_inter == 0 || moge::tile_path_w8_ok(d->d, d->shared_inter));
 }
 
+// The 64-row down tiles are wide (256 columns) when the routed experts can fill
+// several rounds of them: a mean of at least kStreamMaxRows rows per expert (R / N).
+// Below that the launch holds mostly the split shared segment, one round, which
+// narrow tiles spread over more CUs.
+bool wide_down(long long R, int N, int d) {
+  return N > 0 && (double)R / N >= moge::kStreamMaxRows && d % moge::small_down_cols(true) == 0;
+}
+
 // w8: the int8 layer, whose shared segment takes 64-row tiles at every size above
 // the streaming limit
 SharedSplit shared_split(const moge_dims_t* d, bool w8) {
@@ -150,14 +158,16 @@ SharedSplit shared_split(const moge_dims_t* d, bool w8) {
   const int T = d->T, Is = d->shared_inter;
   if (Is == 0 || T <= moge::kSharedStreamMaxRows) return s;
   if (w8 ? !w8_tiles_ok_for(d) : !tiles_ok_for(d)) return s;
-  // 64-row tiles: 64 features (gate/up) or 128 columns (down) per tile; 256-row
-  // tiles: 96 features or 256 columns
+  // 64-row tiles: 64 features (gate/up) or small_down_cols columns (down) per
+  // tile; 256-row tiles: 96 features or 256 columns
   if (w8 || T <= moge::kSharedSmallGateUpRows)
     s.gu = moge::tile_ksplit(T, d->d, Is / 64, 64);
   else
     s.gu = moge::tile_ksplit(T, d->d, Is / 96, 256);
   if (w8 || T <= moge::kSharedSmallDownRows)
-    s.dn = moge::tile_ksplit(T, Is, d->d / 128, 64);
+    s.dn = moge::tile_ksplit(
+        T, Is, d->d / moge::small_down_cols(wide_down((long long)T * d->M * d->k_per_group, d->N, d->d)),
+        64);
   else
     s.dn = moge::tile_ksplit(T, Is, d->d / 256, 256);
   return s;
@@ -294,6 +304,7 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
   const int thr = tiles_ok ? rr.stream_max : INT_MAX;
   const int sh_thr = tiles_ok ? moge::kSharedStreamMaxRows : INT_MAX;
   const int thr_big = rr.small_max;
+  const bool wide = wide_down(routed.rows, routed.n_exp, d);
   routed.thr = thr;
   if (sh) sh->thr = sh_thr;
   const bool sh_stream = sh && sh->rows <= sh_thr;
@@ -341,7 +352,7 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
         if (routed_here) CHECK(hip_check(moge::launch_ffn_tile(gateup, true, d, a, nullptr, st), what));
         CHECK(hip_check(moge::launch_ffn_tile(gateup, true, d, b, nullptr, st), what));
       } else {
-        CHECK(hip_check(moge::launch_ffn_tile(gateup, rg.big, d, a, sh_here ? &b : nullptr, st),
+        CHECK(hip_check(moge::launch_ffn_tile(gateup, rg.big, d, a, sh_here ? &b : nullptr, st, wide),
                         what));
       }
       if (sliced && gateup)
@@ -400,7 +411,8 @@ moge_status_t run_ffn_w8(int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh, h
           b.part = sh_part;
         }
       }
-      CHECK(hip_check(moge::launch_ffn_tile_w8(gateup, d, a, sh_here ? &b : nullptr, st),
+      CHECK(hip_check(moge::launch_ffn_tile_w8(gateup, d, a, sh_here ? &b : nullptr, st,
+                                               wide_down(routed.rows, routed.n_exp, d)),
                       gateup ? "int8 expert gate/up tiles" : "int8 expert down tiles"));
       if (sliced && gateup)
         CHECK(hip_check(moge::launch_swiglu_parts(sh_part, ks, sh->rows, sh->inter, sh->h, st),

@@ -10,9 +10,10 @@
 //         waves 2 (rows) x 2 (weight rows), each 128 rows x (96 | 128) weight rows
 //         as 4 x (3 | 4) blocks of 32x32 float32 accumulators.  This one is bound
 //         by the matrix cores.
-//   small (up to 128 rows): 64 rows x (64 gate/up features | 128 output columns);
-//         all four waves on the same 64 rows, each with its own 32 weight rows.
-//         This one streams each expert's weights once and is bound by HBM.
+//   small (up to 128 rows): 64 rows x (64 gate/up features | 128 or, wide, 256
+//         output columns); all four waves on the same 64 rows, each with its own
+//         32 (wide down: 64) weight rows.  This one streams each expert's weights
+//         once and is bound by HBM.
 // gate/up applies SwiGLU in the epilogue and rounds H once.  The matrix
 // instruction is v_mfma_f32_32x32x16_bf16.
 //
@@ -28,8 +29,8 @@
 // The loads of later stages are spread between the MFMAs of the current one; a
 // stage boundary is a wait for the wave's own loads plus a workgroup barrier.  The
 // big tile keeps 2 activation and 3 weight stages in LDS; the small tile keeps 6 of
-// both, enough bytes in flight to cover HBM latency with one workgroup per CU (on
-// int8 codes 4 of both, two workgroups per CU).
+// both (4 for the wide down tile), enough bytes in flight to cover HBM latency with
+// one workgroup per CU (on int8 codes 4 of both, two workgroups per CU).
 //
 // The tiles of a segment form one list: for every expert in the shape's row range
 // ceil(rows / tile rows) row tiles, each paired with every weight tile.  The list
@@ -61,9 +62,14 @@ constexpr int kSmallW8PerCU = 2;
 constexpr int kSmallW8Depth = 4;
 
 // W8: int8 weight codes (w8_layout.hpp) instead of bf16 weights, small shape only.
-template <bool GATEUP, bool BIG, bool W8 = false> struct TileShape {
+// WIDE: the small down tile with 256 output columns instead of 128.  Its contraction
+// is only the intermediate width, so a launch with many tiles spreads the per-tile
+// selection, pipeline fill and epilogue over more bytes with fewer, wider tiles
+// (T=456: bf16 down 0.245 -> 0.218 ms, int8 0.156 -> 0.144 ms); a launch of one
+// round (the split shared segment of a small batch) keeps more, narrower tiles.
+template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false> struct TileShape {
   static constexpr int kM = BIG ? 256 : 64;                       // rows per tile
-  static constexpr int kWRows = BIG ? (GATEUP ? 192 : 256) : 128;  // weight rows per tile
+  static constexpr int kWRows = BIG ? (GATEUP ? 192 : 256) : (WIDE ? 256 : 128);  // weight rows per tile
   static constexpr int kFeat = kWRows / 2;                         // gate/up features per tile
   static constexpr int kWavesM = BIG ? 2 : 1;                      // waves along the rows
   static constexpr int kWavesN = 4 / kWavesM;
@@ -71,8 +77,12 @@ template <bool GATEUP, bool BIG, bool W8 = false> struct TileShape {
   static constexpr int kBlocksPerTile = kWRows / 32;               // 32-row weight blocks
   static constexpr int kWP = kBlocksPerTile / kWavesN;             // ... per wave
   static constexpr int kPerCU = W8 ? kSmallW8PerCU : 1;            // workgroups per CU
-  static constexpr int kDA = BIG ? 2 : (W8 ? kSmallW8Depth : 6);   // activation stages in LDS
-  static constexpr int kDB = BIG ? 3 : (W8 ? kSmallW8Depth : 6);   // weight stages in LDS
+  // stages in LDS (activations, weights).  The wide tile's stages are bigger (bf16
+  // 40 KiB: 4 deep holds the bytes of 6 narrow stages; int8 24 KiB: 3 deep at two
+  // workgroups per CU)
+  static constexpr int kSmallDepth = W8 ? (WIDE ? 3 : kSmallW8Depth) : (WIDE ? 4 : 6);
+  static constexpr int kDA = BIG ? 2 : kSmallDepth;   // activation stages in LDS
+  static constexpr int kDB = BIG ? 3 : kSmallDepth;   // weight stages in LDS
   static constexpr int kAStageBytes = kM * kLineBytes;
   // B stage: bf16 weights, kWRows / 8 fragments of 1 KiB; int8 codes, kWRows / 16
   // code tiles of 1 KiB (16 rows x 64 codes)
@@ -88,6 +98,7 @@ template <bool GATEUP, bool BIG, bool W8 = false> struct TileShape {
   static_assert(kLdsBytes * kPerCU <= 160 * 1024, "LDS budget");
   static_assert((kALoads + kBLoads) * kEvery <= 4 * kTP * kWP, "loads must fit in a stage");
   static_assert(!(W8 && BIG), "int8 codes use the small shape");
+  static_assert(!WIDE || (!GATEUP && !BIG), "the wide tile is the small down tile");
 };
 
 // 8 int8 codes -> their bf16 values (exact: at most 8 significant bits)
@@ -219,10 +230,10 @@ template <int kM> __device__ __forceinline__ int seg_total_tiles(const TileSeg& 
 // SPLIT (big shape only): every tile computes one slice of the contraction and
 // writes float32 partial sums (a separate instantiation, so that the plain big
 // kernels keep their registers).  The small shape handles both at run time.
-template <bool GATEUP, bool BIG, bool W8, bool SPLIT = false>
+template <bool GATEUP, bool BIG, bool W8, bool SPLIT = false, bool WIDE = false>
 __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
   typedef bf16 E;
-  typedef TileShape<GATEUP, BIG, W8> S;
+  typedef TileShape<GATEUP, BIG, W8, WIDE> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::kLdsBytes];
   char* const ldsA = lds;
   char* const ldsB = lds + S::kDA * S::kAStageBytes;
@@ -628,6 +639,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   }
 }
 
+int small_down_cols(bool wide) {
+  return wide ? TileShape<false, false, false, true>::kWRows : TileShape<false, false>::kWRows;
+}
+
 bool tile_path_ok(int d, int inter) {
   // big tiles: 96-feature gate/up and 256-column down tiles; small tiles: 64 and
   // 128 (implied); 64-element stages
@@ -650,9 +665,9 @@ static long long tile_bound(const TileSeg& g, int kM) {
   return bound;
 }
 
-template <bool GATEUP, bool BIG, bool W8 = false, bool SPLIT = false>
+template <bool GATEUP, bool BIG, bool W8 = false, bool SPLIT = false, bool WIDE = false>
 static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStream_t st) {
-  typedef TileShape<GATEUP, BIG, W8> S;
+  typedef TileShape<GATEUP, BIG, W8, WIDE> S;
   const TileSeg bb = b ? *b : TileSeg{};
   const long long wa = GATEUP ? S::kFeat : S::kWRows;
   const long long nta = (GATEUP ? a.inter / wa : d / wa) * ((!BIG || SPLIT) ? a.ksplit : 1);
@@ -670,7 +685,7 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
   }
   const long long grid = per_xcd * kXcds;
   if (grid > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8, SPLIT>), dim3((unsigned)grid), dim3(kTileThreads),
+  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8, SPLIT, WIDE>), dim3((unsigned)grid), dim3(kTileThreads),
                      0, st, a, bb, d);
   return hipGetLastError();
 }
@@ -686,7 +701,7 @@ int tile_ksplit(int rows, int K, int col_tiles, int tile_rows) {
 }
 
 hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const TileSeg* b,
-                           hipStream_t st) {
+                           hipStream_t st, bool wide) {
   // big tiles with contraction slices: a launch of sliced segments only
   const bool sliced = a.ksplit > 1 || (b && b->ksplit > 1);
   if (big && sliced) {
@@ -695,7 +710,9 @@ hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const
                   : launch_shape<false, true, false, true>(d, a, b, st);
   }
   if (gateup) return big ? launch_shape<true, true>(d, a, b, st) : launch_shape<true, false>(d, a, b, st);
-  return big ? launch_shape<false, true>(d, a, b, st) : launch_shape<false, false>(d, a, b, st);
+  if (big) return launch_shape<false, true>(d, a, b, st);
+  return wide ? launch_shape<false, false, false, false, true>(d, a, b, st)
+              : launch_shape<false, false>(d, a, b, st);
 }
 
 bool tile_path_w8_ok(int d, int inter) {
@@ -705,9 +722,10 @@ bool tile_path_w8_ok(int d, int inter) {
 }
 
 hipError_t launch_ffn_tile_w8(bool gateup, int d, const TileSeg& a, const TileSeg* b,
-                              hipStream_t st) {
-  return gateup ? launch_shape<true, false, true>(d, a, b, st)
-                : launch_shape<false, false, true>(d, a, b, st);
+                              hipStream_t st, bool wide) {
+  if (gateup) return launch_shape<true, false, true>(d, a, b, st);
+  return wide ? launch_shape<false, false, true, false, true>(d, a, b, st)
+              : launch_shape<false, false, true>(d, a, b, st);
 }
 
 }  // namespace moge
