@@ -143,12 +143,20 @@ bool w8_tiles_ok_for(const moge_dims_t* d) {
          (d->shared_inter == 0 || moge::tile_path_w8_ok(d->d, d->shared_inter));
 }
 
-// The 64-row down tiles are wide (256 columns) when the routed experts can fill
-// several rounds of them: a mean of at least kStreamMaxRows rows per expert (R / N).
-// Below that the launch holds mostly the split shared segment, one round, which
-// narrow tiles spread over more CUs.
+// The 64-row tiles are wide (96 gate/up features, 256 down columns) when the routed
+// experts can fill several rounds of them: a mean of at least kStreamMaxRows rows
+// per expert (R / N).  Below that the launch holds mostly the split shared
+// segment, one round, which narrow tiles spread over more CUs.  The widths must
+// divide into wide tiles (the routed and shared widths by 96 features, d by 256).
+bool many_small_tiles(long long R, int N) {
+  return N > 0 && (double)R / N >= moge::kStreamMaxRows;
+}
 bool wide_down(long long R, int N, int d) {
-  return N > 0 && (double)R / N >= moge::kStreamMaxRows && d % moge::small_down_cols(true) == 0;
+  return many_small_tiles(R, N) && d % moge::small_down_cols(true) == 0;
+}
+bool wide_gateup(long long R, int N, int inter, int shared_inter) {
+  const int f = moge::small_gateup_feats(true);
+  return many_small_tiles(R, N) && inter % f == 0 && shared_inter % f == 0;
 }
 
 // w8: the int8 layer, whose shared segment takes 64-row tiles at every size above
@@ -160,14 +168,14 @@ SharedSplit shared_split(const moge_dims_t* d, bool w8) {
   if (w8 ? !w8_tiles_ok_for(d) : !tiles_ok_for(d)) return s;
   // 64-row tiles: 64 features (gate/up) or small_down_cols columns (down) per
   // tile; 256-row tiles: 96 features or 256 columns
+  const long long R = (long long)T * d->M * d->k_per_group;
   if (w8 || T <= moge::kSharedSmallGateUpRows)
-    s.gu = moge::tile_ksplit(T, d->d, Is / 64, 64);
+    s.gu = moge::tile_ksplit(
+        T, d->d, Is / moge::small_gateup_feats(!w8 && wide_gateup(R, d->N, d->inter, Is)), 64);
   else
     s.gu = moge::tile_ksplit(T, d->d, Is / 96, 256);
   if (w8 || T <= moge::kSharedSmallDownRows)
-    s.dn = moge::tile_ksplit(
-        T, Is, d->d / moge::small_down_cols(wide_down((long long)T * d->M * d->k_per_group, d->N, d->d)),
-        64);
+    s.dn = moge::tile_ksplit(T, Is, d->d / moge::small_down_cols(wide_down(R, d->N, d->d)), 64);
   else
     s.dn = moge::tile_ksplit(T, Is, d->d / 256, 256);
   return s;
@@ -304,7 +312,8 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
   const int thr = tiles_ok ? rr.stream_max : INT_MAX;
   const int sh_thr = tiles_ok ? moge::kSharedStreamMaxRows : INT_MAX;
   const int thr_big = rr.small_max;
-  const bool wide = wide_down(routed.rows, routed.n_exp, d);
+  const bool wide_gu = wide_gateup(routed.rows, routed.n_exp, routed.inter, sh ? sh->inter : 0);
+  const bool wide_dn = wide_down(routed.rows, routed.n_exp, d);
   routed.thr = thr;
   if (sh) sh->thr = sh_thr;
   const bool sh_stream = sh && sh->rows <= sh_thr;
@@ -352,7 +361,8 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
         if (routed_here) CHECK(hip_check(moge::launch_ffn_tile(gateup, true, d, a, nullptr, st), what));
         CHECK(hip_check(moge::launch_ffn_tile(gateup, true, d, b, nullptr, st), what));
       } else {
-        CHECK(hip_check(moge::launch_ffn_tile(gateup, rg.big, d, a, sh_here ? &b : nullptr, st, wide),
+        CHECK(hip_check(moge::launch_ffn_tile(gateup, rg.big, d, a, sh_here ? &b : nullptr, st,
+                                              gateup ? wide_gu : wide_dn),
                         what));
       }
       if (sliced && gateup)
@@ -412,7 +422,7 @@ moge_status_t run_ffn_w8(int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh, h
         }
       }
       CHECK(hip_check(moge::launch_ffn_tile_w8(gateup, d, a, sh_here ? &b : nullptr, st,
-                                               wide_down(routed.rows, routed.n_exp, d)),
+                                               !gateup && wide_down(routed.rows, routed.n_exp, d)),
                       gateup ? "int8 expert gate/up tiles" : "int8 expert down tiles"));
       if (sliced && gateup)
         CHECK(hip_check(moge::launch_swiglu_parts(sh_part, ks, sh->rows, sh->inter, sh->h, st),

@@ -136,13 +136,14 @@ struct TileSeg {
   // activation rows every weight tile re-reads out of L2)
   bool nt_weights = false;
 };
-// big: 256-row tiles; otherwise 64-row tiles (wide: 256-column down tiles; needs
-// d % 256 == 0)
+// big: 256-row tiles; otherwise 64-row tiles (wide: 96-feature gate/up tiles,
+// needing a width divisible by 96, or 256-column down tiles, needing d % 256 == 0)
 hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const TileSeg* b,
                            hipStream_t st, bool wide = false);
 // shapes the tile kernels cover (96-feature gate/up tiles, 256-column down tiles)
 bool tile_path_ok(int d, int inter);
 // 64-row tiles on int8 codes (tiles from `thr` rows up), and the shapes they cover
+// (wide: 256-column down tiles; gate/up tiles are always narrow)
 hipError_t launch_ffn_tile_w8(bool gateup, int d, const TileSeg& a, const TileSeg* b,
                               hipStream_t st, bool wide = false);
 bool tile_path_w8_ok(int d, int inter);
@@ -152,8 +153,10 @@ bool tile_path_w8_ok(int d, int inter);
 // 64 per slice.  1 = no split, at most kMaxSlices.  Depends on the sizes only.
 constexpr int kMaxSlices = 8;
 int tile_ksplit(int rows, int K, int col_tiles, int tile_rows = 64);
-// output columns of one 64-row down tile, narrow or wide
+// output columns of one 64-row down tile, and features of one 64-row gate/up tile,
+// narrow or wide
 int small_down_cols(bool wide);
+int small_gateup_feats(bool wide);
 // H = silu(sum of gate partials) * (sum of up partials), slices added in order, bf16
 hipError_t launch_swiglu_parts(const float* part, int ksplit, int rows, int inter, void* h,
                                hipStream_t st);

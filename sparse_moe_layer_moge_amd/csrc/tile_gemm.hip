@@ -10,10 +10,11 @@
 //         waves 2 (rows) x 2 (weight rows), each 128 rows x (96 | 128) weight rows
 //         as 4 x (3 | 4) blocks of 32x32 float32 accumulators.  This one is bound
 //         by the matrix cores.
-//   small (up to 128 rows): 64 rows x (64 gate/up features | 128 or, wide, 256
-//         output columns); all four waves on the same 64 rows, each with its own
-//         32 (wide down: 64) weight rows.  This one streams each expert's weights
-//         once and is bound by HBM.
+//   small (up to 128 rows): 64 rows x (64 gate/up features | 128 output columns);
+//         all four waves on the same 64 rows, each with its own 32 weight rows.
+//         Wide: 64 rows x (96 features, waves 2 (rows) x 2 (weight rows) | 256
+//         columns, each wave 64 weight rows).  This one streams each expert's
+//         weights once and is bound by HBM.
 // gate/up applies SwiGLU in the epilogue and rounds H once.  The matrix
 // instruction is v_mfma_f32_32x32x16_bf16.
 //
@@ -62,25 +63,26 @@ constexpr int kSmallW8PerCU = 2;
 constexpr int kSmallW8Depth = 4;
 
 // W8: int8 weight codes (w8_layout.hpp) instead of bf16 weights, small shape only.
-// WIDE: the small down tile with 256 output columns instead of 128.  Its contraction
-// is only the intermediate width, so a launch with many tiles spreads the per-tile
-// selection, pipeline fill and epilogue over more bytes with fewer, wider tiles
-// (T=456: bf16 down 0.245 -> 0.218 ms, int8 0.156 -> 0.144 ms); a launch of one
-// round (the split shared segment of a small batch) keeps more, narrower tiles.
+// WIDE: small tiles with 96 gate/up features (bf16) or 256 down columns instead of
+// 64 and 128.  A launch with many tiles spreads the fixed per-tile cost (selection,
+// pipeline fill, epilogue) over more bytes with fewer, wider tiles (T=456: bf16
+// down 0.245 -> 0.218 ms, int8 0.156 -> 0.144 ms); a launch of one round (the
+// split shared segment of a small batch) keeps more, narrower tiles.
 template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false> struct TileShape {
   static constexpr int kM = BIG ? 256 : 64;                       // rows per tile
-  static constexpr int kWRows = BIG ? (GATEUP ? 192 : 256) : (WIDE ? 256 : 128);  // weight rows per tile
+  static constexpr int kWRows = (BIG || WIDE) ? (GATEUP ? 192 : 256) : 128;  // weight rows per tile
   static constexpr int kFeat = kWRows / 2;                         // gate/up features per tile
-  static constexpr int kWavesM = BIG ? 2 : 1;                      // waves along the rows
+  static constexpr int kWavesM = (BIG || (WIDE && GATEUP)) ? 2 : 1;  // waves along the rows
   static constexpr int kWavesN = 4 / kWavesM;
   static constexpr int kTP = kM / kWavesM / 32;                    // 32-row blocks per wave
   static constexpr int kBlocksPerTile = kWRows / 32;               // 32-row weight blocks
   static constexpr int kWP = kBlocksPerTile / kWavesN;             // ... per wave
   static constexpr int kPerCU = W8 ? kSmallW8PerCU : 1;            // workgroups per CU
-  // stages in LDS (activations, weights).  The wide tile's stages are bigger (bf16
-  // 40 KiB: 4 deep holds the bytes of 6 narrow stages; int8 24 KiB: 3 deep at two
-  // workgroups per CU)
-  static constexpr int kSmallDepth = W8 ? (WIDE ? 3 : kSmallW8Depth) : (WIDE ? 4 : 6);
+  // stages in LDS (activations, weights).  The wide tiles' stages are bigger and
+  // fit fewer deep (bf16 gate/up 32 KiB x 5, down 40 KiB x 4; int8 down 24 KiB x 3,
+  // two workgroups per CU), about the bytes in flight of the narrow rings
+  static constexpr int kSmallDepth =
+      W8 ? (WIDE ? 3 : kSmallW8Depth) : (WIDE ? (GATEUP ? 5 : 4) : 6);
   static constexpr int kDA = BIG ? 2 : kSmallDepth;   // activation stages in LDS
   static constexpr int kDB = BIG ? 3 : kSmallDepth;   // weight stages in LDS
   static constexpr int kAStageBytes = kM * kLineBytes;
@@ -98,7 +100,7 @@ template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false> struct Tile
   static_assert(kLdsBytes * kPerCU <= 160 * 1024, "LDS budget");
   static_assert((kALoads + kBLoads) * kEvery <= 4 * kTP * kWP, "loads must fit in a stage");
   static_assert(!(W8 && BIG), "int8 codes use the small shape");
-  static_assert(!WIDE || (!GATEUP && !BIG), "the wide tile is the small down tile");
+  static_assert(!WIDE || (!BIG && !(W8 && GATEUP)), "the wide tiles are small tiles");
 };
 
 // 8 int8 codes -> their bf16 values (exact: at most 8 significant bits)
@@ -642,6 +644,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
 int small_down_cols(bool wide) {
   return wide ? TileShape<false, false, false, true>::kWRows : TileShape<false, false>::kWRows;
 }
+int small_gateup_feats(bool wide) {
+  return wide ? TileShape<true, false, false, true>::kFeat : TileShape<true, false>::kFeat;
+}
 
 bool tile_path_ok(int d, int inter) {
   // big tiles: 96-feature gate/up and 256-column down tiles; small tiles: 64 and
@@ -709,7 +714,10 @@ hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const
     return gateup ? launch_shape<true, true, false, true>(d, a, b, st)
                   : launch_shape<false, true, false, true>(d, a, b, st);
   }
-  if (gateup) return big ? launch_shape<true, true>(d, a, b, st) : launch_shape<true, false>(d, a, b, st);
+  if (gateup && big) return launch_shape<true, true>(d, a, b, st);
+  if (gateup)
+    return wide ? launch_shape<true, false, false, false, true>(d, a, b, st)
+                : launch_shape<true, false>(d, a, b, st);
   if (big) return launch_shape<false, true>(d, a, b, st);
   return wide ? launch_shape<false, false, false, false, true>(d, a, b, st)
               : launch_shape<false, false>(d, a, b, st);
@@ -723,6 +731,8 @@ bool tile_path_w8_ok(int d, int inter) {
 
 hipError_t launch_ffn_tile_w8(bool gateup, int d, const TileSeg& a, const TileSeg* b,
                               hipStream_t st, bool wide) {
+  // int8 gate/up tiles stay narrow: the wide ones ran slower (T=456: 0.476 ->
+  // 0.503 ms for the layer)
   if (gateup) return launch_shape<true, false, true>(d, a, b, st);
   return wide ? launch_shape<false, false, true, false, true>(d, a, b, st)
               : launch_shape<false, false, true>(d, a, b, st);
