@@ -229,6 +229,41 @@ template <int kM> __device__ __forceinline__ int seg_total_tiles(const TileSeg& 
   return s;
 }
 
+// A segment of at most 64 experts held across the lanes of a wave: lane e has
+// expert e's row tiles, first row, rows and index of its first row tile.  Built
+// once per workgroup (one round of loads for both segments), so that selecting
+// a tile is a ballot over registers instead of another pass over the offsets.
+struct SegLanes {
+  int nt = 0, lo = 0, cnt = 0, start = 0;
+};
+template <int kM> __device__ __forceinline__ SegLanes seg_lanes(const TileSeg& g, int* total) {
+  const int l = threadIdx.x & 63;
+  SegLanes t;
+  if (l < g.n_exp) t.nt = seg_expert_tiles<kM>(g, l, &t.lo, &t.cnt);
+  int inc = t.nt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (l >= o) inc += v;
+  }
+  t.start = inc - t.nt;
+  *total = __shfl(inc, 63, 64);
+  return t;
+}
+// The expert that owns row tile `mt` (as seg_find_expert, from the lanes)
+__device__ __forceinline__ bool seg_lanes_find(const SegLanes& t, int mt, int* e_out, int* lo_out,
+                                               int* cnt_out, int* first_out, int* nrt_out) {
+  const uint64_t m = __ballot(t.nt > 0 && mt >= t.start && mt < t.start + t.nt);
+  if (!m) return false;
+  const int src = __ffsll((long long)m) - 1;
+  *e_out = src;
+  *first_out = __shfl(t.start, src, 64);
+  *lo_out = __shfl(t.lo, src, 64);
+  *cnt_out = __shfl(t.cnt, src, 64);
+  *nrt_out = __shfl(t.nt, src, 64);
+  return true;
+}
+
 // SPLIT (big shape only): every tile computes one slice of the contraction and
 // writes float32 partial sums (a separate instantiation, so that the plain big
 // kernels keep their registers).  The small shape handles both at run time.
@@ -251,8 +286,18 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   constexpr bool kSliced = !BIG || SPLIT;   // this instantiation handles slices
   const int nta = (GATEUP ? a.inter / S::kFeat : d / S::kWRows) * (kSliced ? a.ksplit : 1);
   const int ntb = b.n_exp ? (GATEUP ? b.inter / S::kFeat : d / S::kWRows) * (kSliced ? b.ksplit : 1) : 0;
-  const int ma = seg_total_tiles<S::kM>(a);
-  const int mb = b.n_exp ? seg_total_tiles<S::kM>(b) : 0;
+  // segments of at most 64 experts: per-lane tables (one round of loads for
+  // both); larger ones are scanned again for every tile
+  const bool lanes = a.n_exp <= 64 && b.n_exp <= 64;
+  SegLanes la, lb;
+  int ma = 0, mb = 0;
+  if (lanes) {
+    la = seg_lanes<S::kM>(a, &ma);
+    if (b.n_exp) lb = seg_lanes<S::kM>(b, &mb);
+  } else {
+    ma = seg_total_tiles<S::kM>(a);
+    mb = b.n_exp ? seg_total_tiles<S::kM>(b) : 0;
+  }
   // every XCD takes an equal share of each segment; the segment with the longer
   // contraction (more work per tile) goes first, so its tiles do not pile up at
   // the end
@@ -283,7 +328,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       // row tile fastest: its R row tiles of one weight tile are neighbouring
       // entries, which run at the same time on the same XCD and share its L2.
       int lo = 0, cnt = 0, first = 0, nrt = 1;
-      if (seg_find_expert<S::kM>(g, t / ntg, &e, &lo, &cnt, &first, &nrt)) {
+      const bool found = lanes ? seg_lanes_find(seg ? lb : la, t / ntg, &e, &lo, &cnt, &first, &nrt)
+                               : seg_find_expert<S::kM>(g, t / ntg, &e, &lo, &cnt, &first, &nrt);
+      if (found) {
         const int j = t - ntg * first;
         const int mt = j % nrt;
         nt = j / nrt;
