@@ -166,8 +166,9 @@ SharedSplit shared_split(const moge_dims_t* d, bool w8) {
   const int T = d->T, Is = d->shared_inter;
   if (Is == 0 || T <= moge::kSharedStreamMaxRows) return s;
   if (w8 ? !w8_tiles_ok_for(d) : !tiles_ok_for(d)) return s;
-  // 64-row tiles: 64 features (gate/up) or small_down_cols columns (down) per
-  // tile; 256-row tiles: 96 features or 256 columns
+  // 64-row tiles: small_gateup_feats features (gate/up) or small_down_cols columns
+  // (down) per tile, narrow or wide as the launch will be; 256-row tiles: 96
+  // features or 256 columns
   const long long R = (long long)T * d->M * d->k_per_group;
   if (w8 || T <= moge::kSharedSmallGateUpRows)
     s.gu = moge::tile_ksplit(
@@ -384,9 +385,11 @@ moge::TileSeg tile_view_w8(const moge::FfnSeg& f, bool gateup) {
 }
 
 // Weight-only int8 experts: experts with at most kStreamMaxRows rows (the shared
-// segment: kSharedStreamMaxRows) stream their codes; larger ones take the int8
-// 64-row tiles, the shared segment with its contraction split when it is small.
-// Without a tile shape for the sizes every expert streams.
+// segment: kSharedStreamMaxRows) stream their codes, unless the mean rows per
+// expert folds that range into the tiles; larger ones take the int8 64-row tiles
+// (wide down tiles when the routed experts fill several rounds), the shared
+// segment with its contraction split when it is small.  Without a tile shape for
+// the sizes every expert streams.
 moge_status_t run_ffn_w8(int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh, hipStream_t st,
                          bool marks, SharedSplit split, float* sh_part) {
   const bool tiles = moge::tile_path_w8_ok(d, routed.inter) &&

@@ -30,15 +30,18 @@
 // The loads of later stages are spread between the MFMAs of the current one; a
 // stage boundary is a wait for the wave's own loads plus a workgroup barrier.  The
 // big tile keeps 2 activation and 3 weight stages in LDS; the small tile keeps 6 of
-// both (4 for the wide down tile), enough bytes in flight to cover HBM latency with
-// one workgroup per CU (on int8 codes 4 of both, two workgroups per CU).
+// both (wide: 5 for gate/up, 4 for down), enough bytes in flight to cover HBM
+// latency with one workgroup per CU (on int8 codes 4 of both, 3 for the wide down
+// tile, two workgroups per CU).
 //
 // The tiles of a segment form one list: for every expert in the shape's row range
-// ceil(rows / tile rows) row tiles, each paired with every weight tile.  The list
-// is built on the device from the expert offsets (no host synchronisation).  Each
-// XCD takes a contiguous eighth of every segment's list, so consecutive entries
-// (same row tile, neighbouring weight tiles) share one L2; the segment with the
-// longer contraction is scheduled first.
+// ceil(rows / tile rows) row tiles, each paired with every weight tile (and
+// contraction slice), row tile fastest inside the expert's block.  The list is
+// built on the device from the expert offsets (no host synchronisation).  Each
+// XCD takes a contiguous eighth of every segment's list, so neighbouring entries
+// (an expert's row tiles of one weight tile, then its next weight tiles) run at
+// the same time on one XCD and share its L2; the segment with the longer
+// contraction is scheduled first.
 #include <limits.h>
 
 #include <type_traits>
@@ -66,8 +69,9 @@ constexpr int kSmallW8Depth = 4;
 // WIDE: small tiles with 96 gate/up features (bf16) or 256 down columns instead of
 // 64 and 128.  A launch with many tiles spreads the fixed per-tile cost (selection,
 // pipeline fill, epilogue) over more bytes with fewer, wider tiles (T=456: bf16
-// down 0.245 -> 0.218 ms, int8 0.156 -> 0.144 ms); a launch of one round (the
-// split shared segment of a small batch) keeps more, narrower tiles.
+// down 0.245 -> 0.218 ms and gate/up 0.381 -> 0.367 ms, int8 down 0.156 ->
+// 0.144 ms); a launch of one round (the split shared segment of a small batch)
+// keeps more, narrower tiles.
 template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false> struct TileShape {
   static constexpr int kM = BIG ? 256 : 64;                       // rows per tile
   static constexpr int kWRows = (BIG || WIDE) ? (GATEUP ? 192 : 256) : 128;  // weight rows per tile
