@@ -90,16 +90,17 @@ hipError_t launch_w8_quantize(const void* src0, const void* src1, int n_exp, int
                               int8_t* dst, float* scale0, float* scale1, hipStream_t st);
 
 // ---- expert FFN, MFMA tile path (tile_gemm.hip, bf16) ----------------------
-// Routed experts with at most kStreamMaxRows rows take the streaming kernels; those
-// with more take 64-row MFMA tiles up to kSmallTileMaxRows rows and 256-row tiles
-// beyond.  The shared experts (one segment of T rows) stream up to
-// kSharedStreamMaxRows and take 64-row tiles up to kSharedSmallGateUpRows (gate/up)
-// or kSharedSmallDownRows (down) and 256-row tiles beyond; a single segment too
-// small to give one tile per CU has its contraction split over several tiles
-// (tile_ksplit), so that it does not re-read its weights once per 64 rows.  A streamed segment of more than 32 rows keeps three or four row
-// subtiles of activations in registers and so few weight steps in flight; the
-// 64-row tiles stage both operands in LDS instead.  The limits are measured
-// choices on MI355X.
+// By default routed experts with at most kStreamMaxRows rows take the streaming
+// kernels; those with more take 64-row MFMA tiles up to kSmallTileMaxRows rows and
+// 256-row tiles beyond (the layer moves these limits by the mean rows per expert).
+// The shared experts (one segment of T rows) stream up to kSharedStreamMaxRows and
+// take 64-row tiles up to kSharedSmallGateUpRows (gate/up) or kSharedSmallDownRows
+// (down) and 256-row tiles beyond; a single segment too small to give one tile per
+// CU has its contraction split over several tiles (tile_ksplit), so that it does
+// not re-read its weights once per 64 rows.  A streamed segment of more than 32
+// rows keeps three or four row subtiles of activations in registers and so few
+// weight steps in flight; the 64-row tiles stage both operands in LDS instead.
+// The limits are measured choices on MI355X.
 constexpr int kStreamMaxRows = 32;
 constexpr int kSharedStreamMaxRows = 32;
 constexpr int kSmallTileMaxRows = 128;
