@@ -465,6 +465,13 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   constexpr int kTP = S::kTP, kWP = S::kWP;
   constexpr int kSub = kTileK / 16;                  // MFMA sub-steps per stage
   const int wm = w % S::kWavesM, wn = w / S::kWavesM;
+  // 32-row blocks of this wave that hold rows of the tile.  A wave with fewer
+  // than kTP runs a second copy of the main loop that skips the MFMAs of the
+  // others (their loads still go out, in bounds, so that the wait counts stay
+  // the same): the last, nearly empty row tile of an expert then costs little
+  // more than streaming its weights once.  The full tiles keep a loop without
+  // the branches, which would otherwise cost them 5-7 %.
+  const int nact = __builtin_amdgcn_readfirstlane(max(0, min(kTP, (rows - wm * kTP * 32 + 31) >> 5)));
   f32x16 acc[kWP][kTP];
 #pragma unroll
   for (int q = 0; q < kWP; ++q)
@@ -502,7 +509,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   // MFMAs of stage kb.  In between go out (one after every kEvery MFMAs, A first)
   // the A loads of stage kb + kDA - 1 when `next_a`, and the B loads of stage
   // kb + kDB - 1 when `next_b`.  Operand fragments are read one sub-step ahead.
-  auto compute = [&](int kb, auto next_a, auto next_b) {
+  auto compute = [&](int kb, auto next_a, auto next_b, auto check) {
     constexpr int na = decltype(next_a)::value ? S::kALoads : 0;
     constexpr int nl = na + (decltype(next_b)::value ? S::kBLoads : 0);
     const char* A = ldsA + (kb % S::kDA) * S::kAStageBytes;
@@ -516,7 +523,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       for (int p = 0; p < kTP; ++p)
 #pragma unroll
         for (int q = 0; q < kWP; ++q) {
-          acc[q][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[h & 1][q], tf[h & 1][p], acc[q][p], 0, 0, 0);
+          if (!decltype(check)::value || p < nact)
+            acc[q][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[h & 1][q], tf[h & 1][p], acc[q][p], 0, 0, 0);
           const int m = (h * kTP + p) * kWP + q;
           const int j = m / S::kEvery;
           if (m % S::kEvery == S::kEvery - 1 && j < nl) {
@@ -556,6 +564,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
       for (int i = 0; i < S::kBLoads; ++i) issue_b(i, s);
     }
   }
+  auto main_loop = [&](auto check) {
   int kb = 0;
   // both operands of a later stage go out
   for (; kb + S::kDB - 1 < nk; ++kb) {
@@ -563,20 +572,25 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
     // every wave's loads of stage kb are in, and every wave has finished reading
     // the buffers the loads issued during this stage overwrite (stage kb - 1's)
     barrier_only();
-    compute(kb, std::true_type{}, std::true_type{});
+    compute(kb, std::true_type{}, std::true_type{}, check);
   }
   // only activations of a later stage go out
   for (; kb + S::kDA - 1 < nk; ++kb) {
     wait_vmcnt_le<kPendSteady>(pending(kb));
     barrier_only();
-    compute(kb, std::true_type{}, std::false_type{});
+    compute(kb, std::true_type{}, std::false_type{}, check);
   }
   // nothing goes out
   for (; kb < nk; ++kb) {
     wait_vmcnt_le<kPendSteady>(pending(kb));
     barrier_only();
-    compute(kb, std::false_type{}, std::false_type{});
+    compute(kb, std::false_type{}, std::false_type{}, check);
   }
+  };
+  if (nact == kTP)
+    main_loop(std::false_type{});
+  else
+    main_loop(std::true_type{});
 
   // ---- epilogue ----------------------------------------------------------------
   // acc[q][p]: lane l, register r holds weight row 8*(r/4) + 4*(l/32) + r%4 of
