@@ -171,9 +171,11 @@ def test_expert_ffn(lib, name, T):
     assert err <= tolerance(cfg), err
 
 
-# Per-expert row counts on both sides of every switch between the kernels: the
-# streaming kernels (up to 32 rows), 64-row tiles (up to 128) and 256-row tiles,
-# with partial tiles of every kind.  The oracle checks sampled rows of every expert.
+# Per-expert row counts on both sides of the switch between the streaming kernels
+# (up to 32 rows) and the 64-row tiles, with partial tiles of every kind.  At a
+# mean under 64 rows per expert the experts of more than 128 rows take 64-row
+# tiles as well; the 256-row tiles are covered below.  The oracle checks sampled
+# rows of every expert.
 BOUNDARY_ROWS = [0, 1, 16, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 513]
 
 
@@ -210,6 +212,53 @@ def test_expert_ffn_row_count_boundaries(lib):
                        inp.w_down, cfg.dtype)
     err = normwise_rel_err(y[pick], ref)
     assert err <= tolerance(cfg), err
+
+
+# Experts of more than 128 rows on 256-row tiles (a mean of 64-256 rows per expert
+# keeps both tile launches), with last row tiles that leave each wave's four
+# 32-row blocks full, partly filled or empty; experts of up to 128 rows on 64-row
+# tiles beside them.  Every 32-row block boundary of each expert's last 288 rows
+# is sampled.
+PARTIAL_TILE_ROWS = [129, 160, 255, 256, 257, 263, 287, 288, 289, 319, 320, 352, 383, 384,
+                     385, 416, 448, 449, 480, 511, 512, 513, 600, 769,
+                     0, 1, 33, 64, 65, 100, 128]
+
+
+def test_expert_ffn_partial_256_row_tiles(lib):
+    import torch
+    cfg = C1
+    rows = list(PARTIAL_TILE_ROWS) + [150] * (cfg.N - len(PARTIAL_TILE_ROWS))
+    rows[-1] += (-sum(rows)) % cfg.K           # total divisible by K
+    counts = np.array(rows, dtype=np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    assert 64 < R / cfg.N < 256
+    T = R // cfg.K
+    inp, dw = layer_inputs(cfg, 64)            # weights only
+    x_perm_h = S.make_x(cfg, T=R, seed=8)
+    dims = dims_of(lib, cfg, T)
+    y_perm = _empty((R, cfg.d), dw["x"].dtype)
+    ws = _empty(lib.workspace_size(dims), torch.uint8)
+    say("expert_ffn partial 256-row tiles", R)
+    lib.expert_ffn(dims, to_dev(x_perm_h, cfg.dtype), to_dev(offsets, "f32"),
+                   dw["w_gate"], dw["w_up"], dw["w_down"], y_perm, ws)
+    torch.cuda.synchronize()
+    y = values(to_host(y_perm))
+    pick, sub_counts = [], []
+    for e in range(cfg.N):
+        lo, c = int(offsets[e]), int(counts[e])
+        sel = {j for j in (0, c // 2, c - 1) if 0 <= j < c}
+        sel |= {j for j in range(max(0, c - 288), c) if j % 32 in (0, 31)}
+        pick += sorted(lo + j for j in sel)
+        sub_counts.append(len(sel))
+    pick = np.array(pick, dtype=np.int64)
+    sub_off = np.concatenate([[0], np.cumsum(sub_counts)]).astype(np.int64)
+    ref = O.expert_ffn(O.to_f64(x_perm_h[pick], cfg.dtype), sub_off, inp.w_gate, inp.w_up,
+                       inp.w_down, cfg.dtype)
+    err = normwise_rel_err(y[pick], ref)
+    assert err <= tolerance(cfg), err
+    # and no row of any expert is left unwritten or non-finite
+    assert np.isfinite(y).all()
 
 
 @pytest.mark.parametrize("name,T", [("C0", 64), ("C1", 64), ("C1", 100)])
