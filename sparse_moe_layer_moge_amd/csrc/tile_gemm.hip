@@ -32,7 +32,9 @@
 // big tile keeps 2 activation and 3 weight stages in LDS; the small tile keeps 6 of
 // both (wide: 5 for gate/up, 4 for down), enough bytes in flight to cover HBM
 // latency with one workgroup per CU (on int8 codes 4 of both, 3 for the wide down
-// tile, two workgroups per CU).
+// tile, two workgroups per CU).  An expert's last row tile is mostly partial: a
+// wave whose 32-row blocks are not all filled runs a copy of the main loop that
+// skips the MFMAs of the empty ones.
 //
 // The tiles of a segment form one list: for every expert in the shape's row range
 // ceil(rows / tile rows) row tiles, each paired with every weight tile (and
