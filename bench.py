@@ -69,11 +69,22 @@ def parse_args():
     return ap.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """Source text without its // comments, trailing blanks and blank lines: the
+    hash follows what the compiler sees, not how the code is explained."""
+    out = []
+    for line in text.splitlines():
+        line = line.split("//", 1)[0].rstrip()
+        if line:
+            out.append(line)
+    return "\n".join(out)
+
+
 def ffn_source_hash(kind: str = "bf16") -> str:
     h = hashlib.sha256()
     for f in FFN_SOURCES[kind]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -62,3 +62,9 @@ def test_more_than_one_gpu_is_refused():
 def test_source_hash_is_stable():
     assert bench.ffn_source_hash("bf16") == bench.ffn_source_hash("bf16")
     assert bench.ffn_source_hash("bf16") != bench.ffn_source_hash("w8")
+
+
+def test_source_hash_ignores_comments_only():
+    code = "int f(int x) {  // doubles\n  return 2 * x;\n}\n"
+    assert bench._code_only(code) == bench._code_only("// note\n" + code.replace("  // doubles", ""))
+    assert bench._code_only(code) != bench._code_only(code.replace("2 * x", "3 * x"))
