@@ -53,7 +53,8 @@ def _draw_tiles(seed):
                    router_std=1.0 / np.sqrt(d), zipf_s=float(rng.choice([0.0, 1.2])), seed=seed)
 
 
-CASES = list(range(24))
+# seeds 0-15: any shape; 16-31: shapes and batches for the tile kernels
+CASES = list(range(32))
 
 # Skewed batches (Zipf(1.2) router bias) at the edges of the host's row-range
 # choice, which uses only the mean rows per expert R / N:
