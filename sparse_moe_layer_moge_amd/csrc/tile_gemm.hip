@@ -511,6 +511,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   // MFMAs of stage kb.  In between go out (one after every kEvery MFMAs, A first)
   // the A loads of stage kb + kDA - 1 when `next_a`, and the B loads of stage
   // kb + kDB - 1 when `next_b`.  Operand fragments are read one sub-step ahead.
+  // With `check`, the MFMAs of the wave's row blocks from nact on are skipped.
   auto compute = [&](int kb, auto next_a, auto next_b, auto check) {
     constexpr int na = decltype(next_a)::value ? S::kALoads : 0;
     constexpr int nl = na + (decltype(next_b)::value ? S::kBLoads : 0);
