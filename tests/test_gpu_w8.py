@@ -16,7 +16,7 @@ import pytest
 
 from oracle import moge_oracle as O
 from synth import inputs as S
-from synth.configs import C0, C1, C2
+from synth.configs import C0, C1, C2, C3
 from tests import packed_ref
 from tests.gpu_util import (dims_of, layer_inputs, normwise_rel_err, say, to_dev, to_host,
                             tolerance, values, weight_key)
@@ -25,7 +25,7 @@ from tests.gpu_util import (dims_of, layer_inputs, normwise_rel_err, say, to_dev
 # and I = 192, I_s = 384 with two experts per group (K = 8)
 W1 = replace(C0, name="W8-small", dtype="bf16")
 W2 = replace(C0, name="W8-small-kp2", dtype="bf16", kp=2, inter=192, shared_inter=384)
-CONFIGS = {"W1": W1, "W2": W2, "C1": C1, "C2": C2}
+CONFIGS = {"W1": W1, "W2": W2, "C1": C1, "C2": C2, "C3": C3}
 
 
 def _empty(shape, dtype):
@@ -134,8 +134,10 @@ def test_w8_layer_small(lib, name, T):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("name,T", [("C1", 64), ("C1", 17), ("C2", 456)])
+@pytest.mark.parametrize("name,T", [("C1", 64), ("C1", 17), ("C2", 456), ("C3", 4096)])
 def test_w8_layer_decode_sizes(lib, name, T):
+    # (the prefill batch too: every routed expert then takes about eight 64-row
+    # tiles on int8 codes, the last one partial)
     cfg = CONFIGS[name]
     inp, dw = layer_inputs(cfg, T)
     scores = S.make_scores(cfg, T=T)
