@@ -154,7 +154,20 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_permute_small(
   const int nchunks = (T + 63) / 64;
   const int32_t* idx = idx_g;
   if constexpr (kCached) {
-    for (int i = threadIdx.x; i < T * K; i += blockDim.x) s_idx[i] = idx_g[i];
+    // every load goes out before the first store, so the copy costs one memory
+    // latency instead of one per pass over the workgroup
+    constexpr int kPasses = (kSmallIdxCache + 64 * kSmallWaves - 1) / (64 * kSmallWaves);
+    int v[kPasses];
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+      const int i = threadIdx.x + j * 64 * kSmallWaves;
+      v[j] = i < T * K ? idx_g[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+      const int i = threadIdx.x + j * 64 * kSmallWaves;
+      if (i < T * K) s_idx[i] = v[j];
+    }
     __syncthreads();
     idx = s_idx;
   }
