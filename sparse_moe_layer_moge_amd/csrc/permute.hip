@@ -4,7 +4,7 @@
 // kernels below reproduce it bit for bit without ordered atomics.  Tokens are
 // handled in chunks of 64, one token per lane:
 //   1. per chunk and expert, how many of the chunk's tokens chose the expert
-//      (popcount of a wave ballot);
+//      (popcount of a wave ballot, or of a mask built with LDS atomic ORs);
 //   2. per expert, an exclusive prefix over chunks, then over experts -> counts,
 //      offsets and per-group loads (every group load equals T*K', the zero
 //      imbalance the grouped routing guarantees: TechWalker page, section 一);
@@ -134,9 +134,10 @@ __device__ __forceinline__ void expert_offsets(const int32_t* cnt, int N, int32_
 }
 
 // ---------------------------------------------------------------------------
-// single workgroup: T <= 64 * kSmallChunks.  The masks and counts are split by
-// (chunk, slice of the experts) and the scatter by (chunk, slot), so that a
-// decode batch of one chunk still spreads over every wave.  kCached: the slot
+// single workgroup: T <= 64 * kSmallChunks.  The masks are built with LDS atomic
+// ORs (one wave per chunk, one per slot: a ballot per expert and chunk took 8 us
+// of the kernel's 15 at T=456), the counts and the scatter are split over every
+// wave by (chunk, expert) and (chunk, slot).  kCached: the slot
 // indices (T * K <= kSmallIdxCache) are copied to LDS first, so that the scatter's
 // reads of them (several units per wave, each a dependent read) cost LDS latency.
 // ---------------------------------------------------------------------------
@@ -172,25 +173,29 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_permute_small(
     idx = s_idx;
   }
 
-  // masks and per-chunk counts: wave w takes chunk w % nchunks and every S-th
-  // expert from w / nchunks on (S waves per chunk)
-  const int S = nchunks > 0 ? max(1, kSmallWaves / nchunks) : 1;
-  if (w < nchunks * S) {
-    const int c = w % nchunks, sl = w / nchunks;
-    uint64_t chosen[4];
-    chosen_set(idx, c * 64 + l, K, N, c * 64 + l < T, chosen);
-    for (int e = sl; e < N; e += S) {
-      const uint64_t m = __ballot(in_set(chosen, e));
-      if (l == 0) {
-        s_mask[c][e] = m;
-        if (nchunks == 1) {  // one chunk: its count is the total, nothing before it
-          s_base[0][e] = 0;
-          s_cnt[e] = __popcll(m);
-          counts[e] = __popcll(m);
-        } else {
-          s_base[c][e] = __popcll(m);
-        }
-      }
+  // masks: bit l of s_mask[c][e] is set when token 64 c + l chose expert e.  Each
+  // chunk's wave ORs its tokens' bits into LDS (one atomic per slot; OR does not
+  // depend on the order), instead of one ballot per expert and chunk
+  for (int i = threadIdx.x; i < nchunks * N; i += blockDim.x) s_mask[i / N][i % N] = 0ull;
+  __syncthreads();
+  if (w < nchunks) {
+    const int t = w * 64 + l;
+    if (t < T)
+      for_each_slot(idx, t, K, [&](int, int e) {
+        if ((unsigned)e < (unsigned)N) atomicOr(&s_mask[w][e], 1ull << l);
+      });
+  }
+  __syncthreads();
+  // per-chunk counts (with one chunk, the totals: nothing comes before it)
+  for (int i = threadIdx.x; i < nchunks * N; i += blockDim.x) {
+    const int c = i / N, e = i - c * N;
+    const int n = __popcll(s_mask[c][e]);
+    if (nchunks == 1) {
+      s_base[0][e] = 0;
+      s_cnt[e] = n;
+      counts[e] = n;
+    } else {
+      s_base[c][e] = n;
     }
   }
   __syncthreads();
