@@ -3,12 +3,12 @@
 // Rows are sorted by expert, then by token, so the result is unique and the
 // kernels below reproduce it bit for bit without ordered atomics.  Tokens are
 // handled in chunks of 64, one token per lane:
-//   1. per chunk and expert, how many of the chunk's tokens chose the expert
-//      (popcount of a wave ballot, or of a mask built with LDS atomic ORs);
+//   1. per chunk and expert, the mask of the chunk's tokens that chose the expert
+//      (built with LDS atomic ORs, one per slot) and its popcount;
 //   2. per expert, an exclusive prefix over chunks, then over experts -> counts,
 //      offsets and per-group loads (every group load equals T*K', the zero
 //      imbalance the grouped routing guarantees: TechWalker page, section 一);
-//   3. per chunk, the ballot masks again; the rank of a token among the chunk's
+//   3. per chunk, the masks again; the rank of a token among the chunk's
 //      tokens that chose expert e is popcount(mask_e & lanes-below-me), so rows
 //      come out in token order.
 // Small batches run in one workgroup (one launch, all counts in LDS); larger ones
@@ -39,29 +39,21 @@ __device__ __forceinline__ void for_each_slot(const int32_t* idx, int t, int K, 
   }
 }
 
-// The set of experts token t chose (entries outside [0, N) and repeats ignored;
-// moge_route never produces either).
-__device__ __forceinline__ void chosen_set(const int32_t* idx, int t, int K, int N,
-                                           bool valid, uint64_t (&chosen)[4]) {
-  chosen[0] = chosen[1] = chosen[2] = chosen[3] = 0ull;
-  if (!valid) return;
-  for_each_slot(idx, t, K, [&](int, int e) {
-    if ((unsigned)e < (unsigned)N) chosen[e >> 6] |= 1ull << (e & 63);
-  });
-}
-
+// whether expert e is in a 256-bit set
 __device__ __forceinline__ bool in_set(const uint64_t (&s)[4], int e) {
   return (s[e >> 6] >> (e & 63)) & 1ull;
 }
 
-// per-expert ballot masks of one chunk (lane 0 writes them)
-__device__ __forceinline__ void chunk_masks(const uint64_t (&chosen)[4], int N,
-                                            uint64_t* __restrict__ masks) {
+// bit l of masks[e] is set when the token of lane l chose expert e (one wave per
+// chunk; masks zeroed before).  LDS atomic ORs, one per slot: the result does not
+// depend on their order, and an expert repeated in a token sets its bit once.
+__device__ __forceinline__ void or_masks(const int32_t* idx, int t, int K, int N, bool valid,
+                                         uint64_t* masks) {
+  if (!valid) return;
   const int l = threadIdx.x & 63;
-  for (int e = 0; e < N; ++e) {
-    const uint64_t m = __ballot(in_set(chosen, e));
-    if (l == 0) masks[e] = m;
-  }
+  for_each_slot(idx, t, K, [&](int, int e) {
+    if ((unsigned)e < (unsigned)N) atomicOr(&masks[e], 1ull << l);
+  });
 }
 
 // rows of one chunk's pairs: row = offsets[e] + base[e] + rank in chunk; slots
@@ -96,21 +88,6 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// How many of one chunk's tokens chose each expert: dst[e] for e < N (one wave).
-__device__ __forceinline__ void chunk_counts(const uint64_t (&chosen)[4], int N,
-                                             int32_t* __restrict__ dst) {
-  const int l = threadIdx.x & 63;
-  for (int q = 0; q * 64 < N; ++q) {
-    int mine = 0;
-    const int n = min(64, N - q * 64);
-    for (int j = 0; j < n; ++j) {
-      const int c = __popcll(__ballot(in_set(chosen, q * 64 + j)));
-      if (l == j) mine = c;
-    }
-    if (l < n) dst[q * 64 + l] = mine;
-  }
-}
-
 // offsets[e] = exclusive prefix of counts over experts (N <= 256, one wave: lane l
 // owns experts 4l .. 4l+3); the total lands in off[N]
 __device__ __forceinline__ void expert_offsets(const int32_t* cnt, int N, int32_t* off) {
@@ -135,9 +112,9 @@ __device__ __forceinline__ void expert_offsets(const int32_t* cnt, int N, int32_
 
 // ---------------------------------------------------------------------------
 // single workgroup: T <= 64 * kSmallChunks.  The masks are built with LDS atomic
-// ORs (one wave per chunk, one per slot: a ballot per expert and chunk took 8 us
-// of the kernel's 15 at T=456), the counts and the scatter are split over every
-// wave by (chunk, expert) and (chunk, slot).  kCached: the slot
+// ORs (one wave per chunk; a wave ballot per expert and chunk, as before, took
+// 8 us of the kernel's 15 at T=456), the counts and the scatter are split over
+// every wave by (chunk, expert) and (chunk, slot).  kCached: the slot
 // indices (T * K <= kSmallIdxCache) are copied to LDS first, so that the scatter's
 // reads of them (several units per wave, each a dependent read) cost LDS latency.
 // ---------------------------------------------------------------------------
@@ -178,13 +155,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_permute_small(
   // depend on the order), instead of one ballot per expert and chunk
   for (int i = threadIdx.x; i < nchunks * N; i += blockDim.x) s_mask[i / N][i % N] = 0ull;
   __syncthreads();
-  if (w < nchunks) {
-    const int t = w * 64 + l;
-    if (t < T)
-      for_each_slot(idx, t, K, [&](int, int e) {
-        if ((unsigned)e < (unsigned)N) atomicOr(&s_mask[w][e], 1ull << l);
-      });
-  }
+  if (w < nchunks) or_masks(idx, w * 64 + l, K, N, w * 64 + l < T, s_mask[w]);
   __syncthreads();
   // per-chunk counts (with one chunk, the totals: nothing comes before it)
   for (int i = threadIdx.x; i < nchunks * N; i += blockDim.x) {
@@ -250,10 +221,14 @@ __global__ __launch_bounds__(64 * kSmallWaves) void k_permute_small(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_chunk_hist(const int32_t* __restrict__ idx, int T, int K,
                                                    int N, int32_t* __restrict__ blk_cnt) {
-  const int t = blockIdx.x * 64 + threadIdx.x;
-  uint64_t chosen[4];
-  chosen_set(idx, t, K, N, t < T, chosen);
-  chunk_counts(chosen, N, blk_cnt + (size_t)blockIdx.x * N);
+  __shared__ uint64_t s_mask[256];
+  const int l = threadIdx.x;
+  const int t = blockIdx.x * 64 + l;
+  for (int e = l; e < N; e += 64) s_mask[e] = 0ull;
+  __syncthreads();
+  or_masks(idx, t, K, N, t < T, s_mask);
+  __syncthreads();
+  for (int e = l; e < N; e += 64) blk_cnt[(size_t)blockIdx.x * N + e] = __popcll(s_mask[e]);
 }
 
 // one workgroup per expert: exclusive prefix of its chunk counts, and its total
@@ -294,16 +269,17 @@ __global__ __launch_bounds__(64) void k_chunk_scatter(const int32_t* __restrict_
   const int t = blockIdx.x * 64 + l;
   // expert offsets from the totals (every workgroup; the first one publishes them)
   expert_offsets(counts, N, s_off);
-  for (int e = l; e < N; e += 64) s_base[e] = blk_base[(size_t)blockIdx.x * N + e];
+  for (int e = l; e < N; e += 64) {
+    s_base[e] = blk_base[(size_t)blockIdx.x * N + e];
+    s_mask[e] = 0ull;
+  }
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int e = l; e <= N; e += 64) offsets[e] = s_off[e];
     const int G = N / M;
     for (int g = l; g < M; g += 64) group_counts[g] = s_off[(g + 1) * G] - s_off[g * G];
   }
-  uint64_t chosen[4];
-  chosen_set(idx, t, K, N, t < T, chosen);
-  chunk_masks(chosen, N, s_mask);
+  or_masks(idx, t, K, N, t < T, s_mask);
   __syncthreads();
   chunk_scatter(idx, t, K, N, t < T, s_off, s_base, s_mask, sorted_pair, pair_row);
 }
