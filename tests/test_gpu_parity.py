@@ -385,10 +385,13 @@ def test_small_bf16_layers(lib, cfg, T):
 
 def _score_error_bound(inp, cfg):
     """Bound on |float32 scores - exact scores| for any summation order:
-    (d + 2) * 2^-24 * sum_j |x_j w_j| (+ one rounding of the bias add)."""
+    (d + 2) * 2^-24 * sum_j |x_j w_j|, plus one rounding of the bias add,
+    2^-24 * (sum_j |x_j w_j| + |b|) (the computed score is at most that in size)."""
     x = O.to_f64(inp.x, cfg.dtype)
     w = O.to_f64(inp.w_router, cfg.dtype)
-    return (cfg.d + 2) * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T) + 1e-30
+    s = np.abs(x) @ np.abs(w).T
+    b = 0.0 if inp.router_bias is None else np.abs(np.asarray(inp.router_bias, np.float64))[None, :]
+    return (cfg.d + 2) * 2.0 ** -24 * s + 2.0 ** -24 * (s + b) + 1e-30
 
 
 @pytest.mark.parametrize("name,T", [("C0", 64), ("C1", 64), ("C2", 456), ("C3", 4096),
@@ -416,6 +419,117 @@ def test_layer_full(lib, name, T):
     same = np.array([t not in set(diff.tolist()) for t in tok])
     err = normwise_rel_err(values(out["y"])[tok][same], ref["y"][same])
     assert err <= tolerance(cfg), err
+
+
+# ----------------------------------------------------------------------------
+# the routed experts alone at full size
+# ----------------------------------------------------------------------------
+# In the layer output the ungated shared experts dominate (the routed part is
+# under a tenth of max|y| at the decode batch), so a normwise bound on y says
+# little about the routed experts.  These run the layer with no shared experts
+# (shared_inter = 0, the same routed weights), so y is the gate-weighted sum of the
+# routed experts alone; the layer reads each row of x through sorted_pair inside
+# the 64-row (T=456) and 256-row (T=4096, 16384) tile kernels at d = 5120.
+
+def _routed_dims(lib, cfg, T):
+    return lib.make_dims(T, cfg.d, cfg.N, cfg.M, cfg.kp, cfg.inter, 0,
+                         lib.MOGE_BF16 if cfg.dtype == "bf16" else lib.MOGE_F32)
+
+
+def _run_routed_layer(lib, cfg, T, dw, scores, packed=None):
+    import torch
+    dims = _routed_dims(lib, cfg, T)
+    y = _empty((T, cfg.d), dw["x"].dtype)
+    idx = _empty((T, dims.K), torch.int32)
+    gc = _empty((cfg.M,), torch.int32)
+    ws = _empty(lib.workspace_size(dims), torch.uint8)
+    if packed is None:
+        lib.layer_forward(dims, dw["x"], None, None, dw["w_gate"], dw["w_up"], dw["w_down"],
+                          None, None, None, y, ws, logits_in=to_dev(scores, "f32"),
+                          topk_idx_out=idx, group_counts_out=gc)
+    else:
+        lib.layer_forward_packed(dims, dw["x"], None, None, packed, y, ws,
+                                 logits_in=to_dev(scores, "f32"), topk_idx_out=idx,
+                                 group_counts_out=gc)
+    torch.cuda.synchronize()
+    return to_host(y), to_host(idx), to_host(gc)
+
+
+def _no_shared(cfg):
+    z = np.zeros((0, cfg.d), dtype=np.uint16 if cfg.dtype == "bf16" else np.float32)
+    return z, z, np.ascontiguousarray(z.T)
+
+
+def elementwise_rel_err(y, ref, floor_frac=1e-2):
+    """Elementwise |y - ref| / |ref| over the elements with |ref| at least
+    floor_frac * max|ref| (a diagnostic beside the normwise measure): max and
+    99.9th percentile."""
+    den = np.abs(ref)
+    m = den >= floor_frac * den.max()
+    r = np.abs(y - ref)[m] / den[m]
+    return float(r.max()), float(np.quantile(r, 0.999))
+
+
+@pytest.mark.parametrize("name,T,n_tok", [("C2", 456, None), ("C3", 4096, 256),
+                                          ("C4", 16384, 256)])
+def test_layer_routed_only_full_size(lib, name, T, n_tok):
+    import torch
+    cfg = CONFIGS[name]
+    inp, dw = layer_inputs(cfg, T)
+    scores = S.make_scores(cfg, T=T)
+    say("layer routed only (row-major)", name, T)
+    y, idx, gc = _run_routed_layer(lib, cfg, T, dw, scores)
+    r = O.route(scores, cfg.M, cfg.kp)
+    np.testing.assert_array_equal(idx, r["idx"])
+    assert (gc == T * cfg.kp).all()
+    # the packed layer gives the same bits
+    dims = _routed_dims(lib, cfg, T)
+    packed = _empty(lib.packed_weights_size(dims), torch.uint8)
+    lib.pack_weights(dims, dw["w_gate"], dw["w_up"], dw["w_down"], None, None, None, packed)
+    say("layer routed only (packed)", name, T)
+    yp, idxp, _ = _run_routed_layer(lib, cfg, T, dw, scores, packed=packed)
+    del packed
+    np.testing.assert_array_equal(idxp, idx)
+    np.testing.assert_array_equal(yp, y)
+    tok = np.arange(T) if n_tok is None else S.sample_tokens(T, n_tok)
+    zg, zu, zd = _no_shared(cfg)
+    ref = O.layer(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down,
+                  zg, zu, zd, M=cfg.M, kp=cfg.kp, dtype=cfg.dtype, logits_f32=scores, tokens=tok)
+    got = values(y)[tok]
+    err = normwise_rel_err(got, ref["y"])
+    emax, e999 = elementwise_rel_err(got, ref["y"])
+    print(f"[routed-only {name}] tokens {len(tok)}: normwise {err:.3e}, elementwise "
+          f"(|ref| >= 1e-2 max) max {emax:.3e}, p99.9 {e999:.3e}", flush=True)
+    assert err <= tolerance(cfg), err
+    assert np.isfinite(values(y)).all()
+
+
+@pytest.mark.parametrize("name,T", [("C2", 456), ("C3", 4096), ("C4", 16384)])
+def test_layer_routed_only_equals_step_path_bitwise(lib, name, T):
+    # the layer's gather through sorted_pair against the step path's materialised
+    # x_perm, with no shared experts: the same kernels on the same rows, bit for bit
+    import torch
+    cfg = CONFIGS[name]
+    _, dw = layer_inputs(cfg, T)
+    scores = S.make_scores(cfg, T=T)
+    say("layer routed only vs step path", name, T)
+    y_layer, _, _ = _run_routed_layer(lib, cfg, T, dw, scores)
+    dims = _routed_dims(lib, cfg, T)
+    ws = _empty(lib.workspace_size(dims), torch.uint8)
+    idx = _empty((T, dims.K), torch.int32)
+    gate = _empty((T, dims.K), torch.float32)
+    lib.route(dims, to_dev(scores, "f32"), idx, gate)
+    i32 = lambda n: _empty(n, torch.int32)
+    counts, offsets, gc, sp, pr = i32(cfg.N), i32(cfg.N + 1), i32(cfg.M), i32(dims.R), i32(dims.R)
+    x_perm = _empty((dims.R, cfg.d), dw["x"].dtype)
+    lib.permute(dims, idx, dw["x"], counts, offsets, gc, sp, pr, x_perm, ws)
+    y_perm = _empty((dims.R, cfg.d), dw["x"].dtype)
+    lib.expert_ffn(dims, x_perm, offsets, dw["w_gate"], dw["w_up"], dw["w_down"], y_perm, ws)
+    del x_perm
+    y = _empty((T, cfg.d), dw["x"].dtype)
+    lib.combine(dims, y_perm, pr, gate, None, y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(y), y_layer)
 
 
 def test_layer_zero_tokens(lib):

@@ -59,6 +59,44 @@ def test_mutant_renormalised_gates(monkeypatch):
     _fails(P.test_layer_equals_dense_brute_force, 1)
 
 
+def test_mutant_router_bias_dropped(monkeypatch):
+    real = O.router_logits
+    monkeypatch.setattr(O, "router_logits", lambda x, w, bias=None: real(x, w, None))
+    _fails(P.test_router_scores_golden_example)
+
+
+def test_mutant_router_bias_sign_flipped(monkeypatch):
+    real = O.router_logits
+    monkeypatch.setattr(O, "router_logits",
+                        lambda x, w, bias=None: real(x, w, None if bias is None else -np.asarray(bias)))
+    _fails(P.test_router_scores_golden_example)
+
+
+def test_mutant_router_bias_after_softmax(monkeypatch):
+    # the bias added to the probabilities after the softmax instead of the scores
+    real_logits, real_softmax = O.router_logits, O.softmax
+    held = {}
+
+    def logits(x, w, bias=None):
+        held["b"] = None if bias is None else np.asarray(bias, dtype=np.float64)
+        return real_logits(x, w, None)
+
+    def softmax(l):
+        p = real_softmax(l)
+        return p if held.get("b") is None else p + held["b"][None, :]
+    monkeypatch.setattr(O, "router_logits", logits)
+    monkeypatch.setattr(O, "softmax", softmax)
+    _fails(P.test_router_scores_golden_example)
+
+
+def test_mutant_router_bias_wrong_index(monkeypatch):
+    real = O.router_logits
+    monkeypatch.setattr(O, "router_logits",
+                        lambda x, w, bias=None: real(x, w, None if bias is None
+                                                     else np.asarray(bias)[::-1].copy()))
+    _fails(P.test_router_scores_golden_example)
+
+
 def test_mutant_silu_sign(monkeypatch):
     monkeypatch.setattr(O, "silu", lambda a: a / (1.0 + np.exp(a)))
     _fails(P.test_silu_closed_forms)

@@ -159,6 +159,44 @@ def test_routing_golden_example():
     assert O.global_topk(scores, 3)[0].tolist() == ex["global_top3_row0"]
 
 
+def test_router_scores_golden_example():
+    # S0 with a per-expert bias: hand-worked integer scores, and a bias that flips
+    # one group's choice for each token (tests/golden/router_scores_small.json)
+    with open(os.path.join(GOLDEN, "router_scores_small.json")) as f:
+        gd = json.load(f)
+    ex = gd["expected"]
+    x = np.array(gd["x"], dtype=np.float32)
+    w = np.array(gd["w_router"], dtype=np.float32)
+    b = np.array(gd["bias"], dtype=np.float32)
+    M, kp = gd["M"], gd["kp"]
+    # scores, exactly (small integers)
+    assert O.router_logits(x.astype(np.float64), w.astype(np.float64)).tolist() == \
+        ex["scores_no_bias"]
+    assert O.router_logits(x.astype(np.float64), w.astype(np.float64), b).tolist() == \
+        ex["scores_with_bias"]
+    # the same scores by an element loop over the stored integers
+    for t in range(2):
+        for e in range(8):
+            v = sum(gd["x"][t][j] * gd["w_router"][e][j] for j in range(3))
+            assert ex["scores_no_bias"][t][e] == v
+            assert ex["scores_with_bias"][t][e] == v + gd["bias"][e]
+    # through the whole layer: the bias goes in before the softmax and the selection
+    N, d, I = 8, 3, 2
+    z = np.zeros
+    for bias, key in ((None, "no_bias"), (b, "with_bias")):
+        out = O.layer(x, w, bias, z((N, I, d), np.float32), z((N, I, d), np.float32),
+                      z((N, d, I), np.float32), z((2, d), np.float32), z((2, d), np.float32),
+                      z((d, 2), np.float32), M=M, kp=kp, dtype="f32")
+        assert out["logits64"].tolist() == ex["scores_" + key]
+        assert out["idx"].tolist() == ex["idx_" + key]
+        assert (out["y"] == 0).all()
+    e = math.e
+    g0 = e ** 2 / (3 * e + 2 * e ** 2 + e ** -3 + 1 + e ** -1)
+    g1 = e ** 6 / (2 + 2 * e ** 4 + e ** 6 + e ** 3 + e ** -1 + e ** -4)
+    np.testing.assert_allclose(out["gate"][0], [g0, g0], rtol=1e-6)
+    np.testing.assert_allclose(out["gate"][1], [g1, g1 / e ** 2], rtol=1e-6)
+
+
 def test_gate_is_unnormalised_global_probability():
     # the gate is the probability from the softmax over all N experts, so the K
     # gates of a token sum to less than 1 when K < N
