@@ -1,24 +1,29 @@
 #!/usr/bin/env python3
 """Throughput of the MoGE expert-layer forward pass on one MI355X.
 
-One step = one moge_layer_forward call over one batch: router scores, global
-softmax, per-group top-K', permutation, routed SwiGLU experts, shared experts and
-the gate-weighted combine.  Inputs are seeded synthetic tensors already resident
-in HBM when the timed region starts.
+One step = one moge_layer_forward_packed call over one batch: router scores,
+global softmax, per-group top-K', permutation, routed SwiGLU experts, shared
+experts and the gate-weighted combine.  Inputs are seeded synthetic tensors
+already resident in HBM when the timed region starts.
 
-Prints ONE JSON line (the default workload is the decode batch of 64 tokens on
-the Pangu-Pro-shaped layer: d=5120, 64 experts in 8 groups, 1 per group, 4 shared
-experts, SwiGLU width 1344, bf16).  The line carries
-  * value: layer tokens/s over the K timed steps (wall clock around them);
-  * roofline: for the dominant kernel (gate/up + SwiGLU of routed and shared
-    experts), its algorithmic bytes (HBM-bound workloads) or flops (MFMA-bound
-    ones) per launch over its mean launch time, from the two HIP events the
-    library records on its own stream around that launch in every timed step;
-  * stages_ms: per-stage means from a few extra, untimed steps that record every
-    stage event;
+The layer is Pangu-Pro-shaped (d=5120, 64 experts in 8 groups, 1 per group, 4
+shared experts, SwiGLU width 1344, bf16).  The headline workload is the largest
+batch, 16384 tokens with a Zipf(1.2) router bias (bound by the matrix cores);
+the same run times the decode batches of 64 and 456 tokens (bound by HBM) and
+the 2 x 2048-token prefill on the same weights and reports them under
+other_workloads.  Prints ONE JSON line; for every workload:
+  * value: layer tokens/s over the K timed steps (host clock around them);
+  * roofline: the dominant kernel (gate/up + SwiGLU of the routed and shared
+    experts): its algorithmic flops (MFMA-bound workloads) or bytes (HBM-bound
+    ones) per launch over its mean launch time, from HIP events the library
+    records on its own stream around that launch in every timed step;
+  * roofline_experts: the same for the routed and shared experts as a whole
+    (gate/up and down stages);
+  * layer_ms_events, stages_ms: per-step layer times (p10/p50/p90) and stage
+    means from extra, untimed steps that record every stage event;
   * cpu_baseline: the CPU oracle timed on the host on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C1]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C4] [--extra C1,C2,C3]
 """
 from __future__ import annotations
 
@@ -53,7 +58,12 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="C1", help="workload: C0..C4 (default C1)")
+    ap.add_argument("--config", default=None,
+                    help="headline workload: C0..C4 (default C4; C1 with --w8)")
+    ap.add_argument("--extra", default=None,
+                    help="comma-separated workloads of the same layer timed in the same run "
+                         "and reported under other_workloads (default with the C4 headline: "
+                         "C1,C2,C3; 'none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
                     help="first run 3 plain device copies of MIB MiB (a reference of known "
@@ -132,9 +142,13 @@ def algorithmic_work(cfg, counts, w8: bool = False):
                    flops=4 * R * d * I + 4 * T * d * Is)
     down = dict(bytes=active * dn_w + sdn_w + (R * I + T * Is) * es + (R + T) * d * es,
                 flops=2 * R * d * I + 2 * T * d * Is)
+    # S4-S6, the routed and shared experts: their weights, x in and y out (the
+    # intermediates H and y_perm are not counted: the method does not need them)
+    experts = dict(bytes=active * (gu_w + dn_w) + sgu_w + sdn_w + 2 * T * d * es,
+                   flops=6 * R * d * I + 6 * T * d * Is)
     layer = dict(bytes=active * (gu_w + dn_w) + sgu_w + sdn_w + N * d * es + 2 * T * d * es,
                  flops=2 * T * d * N + 6 * R * d * I + 6 * T * d * Is)
-    return dict(gate_up=gate_up, down=down, layer=layer, active_experts=active)
+    return dict(gate_up=gate_up, down=down, experts=experts, layer=layer, active_experts=active)
 
 
 def cpu_baseline(cfg, inp, n_tokens: int, min_seconds: float = 10.0, w8=None):
@@ -142,15 +156,18 @@ def cpu_baseline(cfg, inp, n_tokens: int, min_seconds: float = 10.0, w8=None):
     (the int8-weight layer when w8 holds codes and scales)."""
     import numpy as np
     from oracle import moge_oracle as O
+    pools = []
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        pools = [(p.get("internal_api", "?"), int(p.get("num_threads", 1)))
+                 for p in threadpool_info()]
     except Exception:
-        threads = 1
+        pass
+    threads = max([n for _, n in pools] or [1])
     tok = np.arange(min(n_tokens, cfg.T))
     reps = 0
     t0 = time.perf_counter()
-    while True:   # repeat the same call until about 10 s of CPU work (at most 30 calls)
+    while True:   # repeat the same call until about min_seconds of CPU work (at most 30 calls)
         if w8 is None:
             O.layer(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down,
                     inp.ws_gate, inp.ws_up, inp.ws_down, M=cfg.M, kp=cfg.kp, dtype=cfg.dtype,
@@ -165,10 +182,167 @@ def cpu_baseline(cfg, inp, n_tokens: int, min_seconds: float = 10.0, w8=None):
         if dt >= min_seconds or reps >= 30:
             break
     return {"value": reps * len(tok) / dt, "unit": "tokens/s", "cores": int(threads),
+            "host_cpu_count": os.cpu_count(), "blas_pools": pools,
             "kind": "oracle",
             "sample": f"{reps} calls, each {len(tok)} of the batch's {cfg.T} tokens through the "
                       f"whole layer (routing over all {cfg.T} tokens), numpy float64, "
                       f"{dt:.1f} s in total"}
+
+
+def _pcts(a):
+    import numpy as np
+    a = np.asarray(a, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 4), "p50": round(float(np.median(a)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+def stored_traffic(workload: str, w8: bool):
+    """The gate/up stage's HBM bytes per layer step from the committed counter runs,
+    while the kernel sources they were taken on are unchanged (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f).get(f"gate_up@{workload}")
+        if tr and tr.get("source_hash") == ffn_source_hash("w8" if w8 else "bf16"):
+            return tr["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def roofline(bound, dtype, work, t_mean_ms, t_ms, kernel):
+    if bound == "hbm":
+        achieved = work["bytes"] / (t_mean_ms * 1e-3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = work["flops"] / (t_mean_ms * 1e-3) / 1e12
+        peak = MFMA_BF16_PEAK_TFLOPS if dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        unit = "TFLOP/s"
+    return {"bound": bound, "kernel": kernel, "achieved": round(achieved, 1), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4),
+            "algorithmic_bytes": work["bytes"], "algorithmic_flops": work["flops"],
+            "mean_launch_ms": round(t_mean_ms, 4), "launch_ms": _pcts(t_ms)}
+
+
+def run_workload(moge, hip, cfg, w, packed, args, w8_host=None):
+    """Time one workload on the shared device weights; returns its record."""
+    import numpy as np
+    import torch
+    from synth import inputs as S
+
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    t_setup = time.perf_counter()
+    x = dev(S.make_x(cfg))
+    bias = dev(S.zipf_bias(cfg.N, cfg.zipf_s)) if cfg.zipf_s > 0 else None
+    dims = moge.make_dims(cfg.T, cfg.d, cfg.N, cfg.M, cfg.kp, cfg.inter, cfg.I_s,
+                          moge.MOGE_BF16 if cfg.dtype == "bf16" else moge.MOGE_F32)
+    ws = torch.empty(moge.workspace_size(dims), dtype=torch.uint8, device="cuda")
+    y = torch.empty((cfg.T, cfg.d), dtype=tdt, device="cuda")
+    idx = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda")
+    gc = torch.empty((cfg.M,), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    def step():
+        if args.w8:
+            moge.layer_forward_w8(dims, x, w["w_router"], bias, packed, y, ws,
+                                  topk_idx_out=idx, group_counts_out=gc)
+        elif args.row_major:
+            moge.layer_forward(dims, x, w["w_router"], bias, w["w_gate"], w["w_up"],
+                               w["w_down"], w["ws_gate"], w["ws_up"], w["ws_down"], y, ws,
+                               topk_idx_out=idx, group_counts_out=gc)
+        else:
+            moge.layer_forward_packed(dims, x, w["w_router"], bias, packed, y, ws,
+                                      topk_idx_out=idx, group_counts_out=gc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed steps: the library records three events per step on its own stream,
+    # around the gate/up stage (the dominant kernel) and the down stage; each
+    # recorded event costs a few microseconds of GPU time.
+    K = args.steps
+    ev = [[hip.event() for _ in range(3)] for _ in range(K)]
+    marks = [[None] * moge.STAGE_EVENTS for _ in range(K)]
+    for i in range(K):
+        marks[i][3], marks[i][4], marks[i][5] = ev[i]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        moge.set_stage_events(marks[i])
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    moge.set_stage_events(None)
+    gu_ms = np.array([hip.elapsed_ms(e[0], e[1]) for e in ev])
+    dn_ms = np.array([hip.elapsed_ms(e[1], e[2]) for e in ev])
+    ex_ms = np.array([hip.elapsed_ms(e[0], e[2]) for e in ev])
+    for e in ev:
+        for h in e:
+            hip.destroy(h)
+
+    # Stage breakdown and per-step layer times: a separate, untimed pass with every
+    # stage event recorded.
+    n_st = min(K, 20)
+    evs = [[hip.event() for _ in range(moge.STAGE_EVENTS)] for _ in range(n_st)]
+    for i in range(n_st):
+        moge.set_stage_events(evs[i])
+        step()
+    torch.cuda.synchronize()
+    moge.set_stage_events(None)
+    stage_ms = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(moge.STAGE_EVENTS - 1)]
+                         for e in evs])
+    layer_ms = np.array([hip.elapsed_ms(e[0], e[-1]) for e in evs])
+    for e in evs:
+        for h in e:
+            hip.destroy(h)
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=cfg.N)
+    gcounts = gc.cpu().numpy()
+    del ws, y, x
+    torch.cuda.empty_cache()
+
+    work = algorithmic_work(cfg, counts, w8=args.w8)
+    workload = cfg.name + ("-w8a16" if args.w8 else "")
+    ms_per_step = 1e3 * elapsed / K
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    intensity = work["layer"]["flops"] / work["layer"]["bytes"]
+    bound = "mfma" if intensity > ridge else "hbm"
+    gu_kernel = ("gate/up + SwiGLU launch of the routed and shared experts (one 256-row MFMA "
+                 "tile launch at this size)" if bound == "mfma" else
+                 "gate/up + SwiGLU stage of the routed and shared experts (every kernel "
+                 "between the library's two stage events)")
+    rl = roofline(bound, cfg.dtype, work["gate_up"], float(gu_ms.mean()), gu_ms, gu_kernel)
+    rl["traffic"] = stored_traffic(workload, args.w8)
+    rl["traffic_source"] = ("stored: rocprofv3 FETCH_SIZE + WRITE_SIZE of this workload's "
+                            "gate/up kernels (profiles/hbm_traffic.json), scaled by a 1 GiB "
+                            "copy; taken on the current kernel sources" if rl["traffic"] else
+                            "none for the current kernel sources")
+    rl_ex = roofline(bound, cfg.dtype, work["experts"], float(ex_ms.mean()), ex_ms,
+                     "routed and shared experts, S4-S6 (gate/up + SwiGLU and down stages)")
+    return {
+        "workload": workload, "T": cfg.T, "value": round(cfg.T * K / elapsed, 1),
+        "unit": "tokens/s", "ms_per_step": round(ms_per_step, 4),
+        "layer_ms_events": _pcts(layer_ms),
+        "roofline": rl, "roofline_experts": rl_ex,
+        "stages_ms": {n: round(float(v), 4) for n, v in zip(moge.STAGE_NAMES, stage_ms.mean(0))},
+        "down_ms": _pcts(dn_ms),
+        "layer": {"algorithmic_bytes": work["layer"]["bytes"],
+                  "algorithmic_flops": work["layer"]["flops"],
+                  "hbm_GBps": round(work["layer"]["bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+                  "tflops": round(work["layer"]["flops"] / (ms_per_step * 1e-3) / 1e12, 2),
+                  "active_experts": work["active_experts"],
+                  "rows_per_expert_min_max": [int(counts.min()), int(counts.max())],
+                  "imbalance_score": float(gcounts.max() - gcounts.min()) / cfg.T},
+        "setup_s": round(setup_s, 1),
+    }
 
 
 def main() -> int:
@@ -187,10 +361,27 @@ def main() -> int:
     from synth import inputs as S
     from synth.configs import CONFIGS
 
-    cfg = CONFIGS[args.config]
+    head = args.config or ("C1" if args.w8 else "C4")
+    cfg = CONFIGS[head]
+    if args.extra is None:
+        extra = ["C1", "C2", "C3"] if (head == "C4" and not args.w8) else []
+    else:
+        extra = [c for c in args.extra.split(",") if c and c != "none"]
+    extra = [c for c in extra if c != head]
+    for c in extra:
+        o = CONFIGS[c]
+        if (o.d, o.N, o.M, o.kp, o.inter, o.I_s, o.dtype) != (cfg.d, cfg.N, cfg.M, cfg.kp,
+                                                                cfg.inter, cfg.I_s, cfg.dtype):
+            print(json.dumps({"error": f"workload {c} does not share {head}'s layer"}))
+            return 2
+    if args.w8 and cfg.dtype != "bf16":
+        print(json.dumps({"error": "int8 expert weights take bf16 activations"}))
+        return 2
+
+    # the layer's weights: drawn, uploaded and packed once, outside every timed
+    # region, and shared by the workloads (they differ only in x, T and the bias)
     t_setup = time.perf_counter()
-    inp = S.make_layer_inputs(cfg)
-    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    wh = S.make_weights(cfg)
 
     def dev(a):
         if a is None:
@@ -199,21 +390,11 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    x = dev(inp.x)
-    w = {k: dev(getattr(inp, k)) for k in ("w_router", "router_bias", "w_gate", "w_up", "w_down",
-                                           "ws_gate", "ws_up", "ws_down")}
+    w = {k: dev(v) for k, v in wh.items() if k != "router_bias"}
     dims = moge.make_dims(cfg.T, cfg.d, cfg.N, cfg.M, cfg.kp, cfg.inter, cfg.I_s,
                           moge.MOGE_BF16 if cfg.dtype == "bf16" else moge.MOGE_F32)
-    ws = torch.empty(moge.workspace_size(dims), dtype=torch.uint8, device="cuda")
-    y = torch.empty((cfg.T, cfg.d), dtype=tdt, device="cuda")
-    idx = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda")
-    gc = torch.empty((cfg.M,), dtype=torch.int32, device="cuda")
-    # weights are parameters: packed once, outside the timed region
     w8_host = None
     if args.w8:
-        if cfg.dtype != "bf16":
-            print(json.dumps({"error": "int8 expert weights take bf16 activations"}))
-            return 2
         w8_host = S.make_w8_weights(cfg)
         q = {k: dev(v) for k, v in w8_host.items()}
         packed = torch.empty(moge.w8_weights_size(dims), dtype=torch.uint8, device="cuda")
@@ -225,20 +406,12 @@ def main() -> int:
         packed = torch.empty(moge.packed_weights_size(dims), dtype=torch.uint8, device="cuda")
         moge.pack_weights(dims, w["w_gate"], w["w_up"], w["w_down"], w["ws_gate"], w["ws_up"],
                           w["ws_down"], packed)
+    if not args.row_major and not args.w8:
+        for k in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+            w[k] = None          # the packed layer reads only the packed buffer
+        torch.cuda.empty_cache()
     torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t_setup
-
-    def step():
-        if args.w8:
-            moge.layer_forward_w8(dims, x, w["w_router"], w["router_bias"], packed, y, ws,
-                                  topk_idx_out=idx, group_counts_out=gc)
-        elif args.row_major:
-            moge.layer_forward(dims, x, w["w_router"], w["router_bias"], w["w_gate"], w["w_up"],
-                               w["w_down"], w["ws_gate"], w["ws_up"], w["ws_down"], y, ws,
-                               topk_idx_out=idx, group_counts_out=gc)
-        else:
-            moge.layer_forward_packed(dims, x, w["w_router"], w["router_bias"], packed, y, ws,
-                                      topk_idx_out=idx, group_counts_out=gc)
+    weights_s = time.perf_counter() - t_setup
 
     if args.copy_ref > 0:
         src = torch.empty(args.copy_ref << 20, dtype=torch.uint8, device="cuda")
@@ -248,107 +421,47 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     hip = Hip()
-    K = args.steps
-    # Timed steps: the library records only the two events around the gate/up stage
-    # (the roofline kernel) in every step; each recorded event costs GPU time.
-    GU0, GU1 = 3, 4
-    gu = [(hip.event(), hip.event()) for _ in range(K)]
-    marks = [[None] * moge.STAGE_EVENTS for _ in range(K)]
-    for i in range(K):
-        marks[i][GU0], marks[i][GU1] = gu[i]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        moge.set_stage_events(marks[i])
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    moge.set_stage_events(None)
-    gate_up_ms = np.array([hip.elapsed_ms(a, b) for a, b in gu])
-    for a, b in gu:
-        hip.destroy(a)
-        hip.destroy(b)
+    recs = {}
+    for name in [head] + extra:
+        recs[name] = run_workload(moge, hip, CONFIGS[name], w, packed, args, w8_host)
 
-    # Stage breakdown: a separate, untimed pass with every stage event recorded.
-    n_st = min(K, 20)
-    evs = [[hip.event() for _ in range(moge.STAGE_EVENTS)] for _ in range(n_st)]
-    for i in range(n_st):
-        moge.set_stage_events(evs[i])
-        step()
-    torch.cuda.synchronize()
-    moge.set_stage_events(None)
-    stage_ms = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(moge.STAGE_EVENTS - 1)]
-                         for e in evs])
-    for e in evs:
-        for h in e:
-            hip.destroy(h)
-    mean_stage = stage_ms.mean(axis=0)
-    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=cfg.N)
-    gcounts = gc.cpu().numpy()
-    work = algorithmic_work(cfg, counts, w8=args.w8)
-    workload = cfg.name + ("-w8a16" if args.w8 else "")
-
-    ms_per_step = 1e3 * elapsed / K
-    value = cfg.T * K / elapsed
-    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    intensity = work["layer"]["flops"] / work["layer"]["bytes"]
-    bound = "mfma" if intensity > ridge else "hbm"
-    t_gu = float(gate_up_ms.mean()) * 1e-3
-    if bound == "hbm":
-        achieved = work["gate_up"]["bytes"] / t_gu / 1e9
-        peak, unit = HBM_PEAK_GBS, "GB/s"
+    # CPU oracle baselines (host only, after every GPU run)
+    if not args.no_cpu_baseline:
+        for name in [head] + extra:
+            c = CONFIGS[name]
+            inp = S.make_layer_inputs(c, weights=wh)
+            n = args.cpu_tokens if args.cpu_tokens > 0 else min(c.T, 64)
+            recs[name]["cpu_baseline"] = cpu_baseline(c, inp, n, w8=w8_host,
+                                                      min_seconds=10.0 if name == head else 6.0)
     else:
-        achieved = work["gate_up"]["flops"] / t_gu / 1e12
-        peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-        unit = "TFLOP/s"
-    traffic = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f).get(f"gate_up@{workload}")
-        if tr and tr.get("source_hash") == ffn_source_hash("w8" if args.w8 else "bf16"):
-            traffic = tr["bytes_per_launch"]
-    except (OSError, ValueError):
-        pass
+        for name in recs:
+            recs[name]["cpu_baseline"] = None
 
+    h = recs[head]
     rec = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "metric": METRIC, "value": h["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic (seeded N(0,std) inputs, random-init weights)",
-        "config": {"workload": workload, "T": cfg.T, "d": cfg.d, "N": cfg.N, "M": cfg.M,
+        "config": {"workload": h["workload"], "T": cfg.T, "d": cfg.d, "N": cfg.N, "M": cfg.M,
                    "k_per_group": cfg.kp, "inter": cfg.inter, "shared_experts": cfg.n_shared,
-                   "shared_inter_total": cfg.I_s, "parallelism": "single GPU",
+                   "shared_inter_total": cfg.I_s, "zipf_bias": cfg.zipf_s,
+                   "parallelism": "single GPU",
                    "weights": ("int8 codes, float32 per-row scales" if args.w8 else
                                "row-major" if args.row_major else "packed")},
-        "roofline": {"bound": bound,
-                     "kernel": "gate/up + SwiGLU stage (routed and shared experts: every "
-                               "kernel between the two stage events)",
-                     "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                     "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "algorithmic_bytes": work["gate_up"]["bytes"],
-                     "algorithmic_flops": work["gate_up"]["flops"],
-                     "mean_launch_ms": round(float(gate_up_ms.mean()), 4)},
-        "stages_ms": {n: round(float(v), 4) for n, v in zip(moge.STAGE_NAMES, mean_stage)},
-        "stages_note": f"stage means from {n_st} extra untimed steps with all stage events",
-        "layer": {"algorithmic_bytes": work["layer"]["bytes"],
-                  "algorithmic_flops": work["layer"]["flops"],
-                  "hbm_GBps": round(work["layer"]["bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
-                  "tflops": round(work["layer"]["flops"] / (ms_per_step * 1e-3) / 1e12, 2),
-                  "active_experts": work["active_experts"],
-                  "rows_per_expert_min_max": [int(counts.min()), int(counts.max())],
-                  "imbalance_score": float(gcounts.max() - gcounts.min()) / cfg.T},
-        "setup_s": round(setup_s, 1),
+        "roofline": h["roofline"],
+        "cpu_baseline": h["cpu_baseline"],
     }
-    if not args.no_cpu_baseline:
-        n = args.cpu_tokens if args.cpu_tokens > 0 else min(cfg.T, 64)
-        rec["cpu_baseline"] = cpu_baseline(cfg, inp, n, w8=w8_host)
-    else:
-        rec["cpu_baseline"] = None
+    for k in ("roofline_experts", "layer_ms_events", "stages_ms", "down_ms", "layer", "setup_s"):
+        rec[k] = h[k]
+    rec["weights_setup_s"] = round(weights_s, 1)
+    rec["timing_note"] = ("value = tokens/s over the K timed steps by the host clock, "
+                          "synchronised on both sides; launch and stage times from HIP events "
+                          "the library records on its stream; layer_ms_events from "
+                          f"{min(args.steps, 20)} extra steps with every stage event")
+    if extra:
+        rec["other_workloads"] = {recs[n]["workload"]: recs[n] for n in extra}
     print(json.dumps(rec), flush=True)
     return 0
 

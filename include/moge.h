@@ -39,7 +39,9 @@
  *     moge_workspace_size() -> MOGE_ERR_WORKSPACE; a failed kernel launch ->
  *     MOGE_ERR_HIP. In every error case nothing has been enqueued. T = 0 returns
  *     MOGE_OK and enqueues nothing.
- *   - Limits: N <= 256, K = M*K' <= 64, d, I and I_s multiples of 32, T*K < 2^31,
+ *   - Limits: N <= 256, K = M*K' <= 64, d, I and I_s multiples of 32 (one MFMA
+ *     operand fragment spans 32 contraction elements, and every kernel reads whole
+ *     fragments), T*K < 2^31,
  *     and under 4 GiB each: every activation buffer ([T*K, d], [T*K, I], [T, I_s])
  *     and one expert's gate and up weights together (2*I*d elements; 2*I_s*d for
  *     the shared experts), which the kernels address with 32-bit offsets.
@@ -104,7 +106,12 @@ moge_status_t moge_route(const moge_dims_t* dims, const float* logits, float* pr
                          int32_t* topk_idx, float* topk_gate, void* stream);
 
 /* Permutation of the T*K (token, slot) pairs into expert-contiguous order: rows
- * sorted by expert, then by token; pair p = t*K + k.
+ * sorted by expert, then by token; pair p = t*K + k.  Grouped routing gives every
+ * expert group the same number of pairs (TechWalker page, section 一: with K'
+ * experts taken per group, each device's load is T*K'); group_counts exposes it,
+ * so the zero imbalance score can be checked per group.  The pages do not fix the
+ * order of the rows inside an expert; token ascending (a stable counting sort) is
+ * this library's choice, and it makes the permutation unique and bit-exact.
  *   topk_idx     [T,K] int32 in
  *   x            [T,d] dtype in
  *   counts       [N]   int32 out     rows per expert
@@ -137,18 +144,27 @@ moge_status_t moge_expert_ffn(const moge_dims_t* dims, const void* x_perm,
                               const void* w_down, void* y_perm, void* ws, size_t ws_bytes,
                               void* stream);
 
-/* Gate-weighted combine back to token order:
+/* Gate-weighted combine back to token order (TechWalker page, section 一: a
+ * token's output is the sum of its chosen experts' outputs weighted by their
+ * probabilities from the softmax over all experts; mokono.cn 核心亮点 1: the
+ * shared experts are always on and join the sum with weight 1):
  *   y[t] = shared_out[t] + sum_{k=0..K-1} topk_gate[t,k] * y_perm[pair_row[t*K+k]]
- * summed in float32 in slot order, rounded once to dtype.
+ * summed in float32 in slot order (the pages give no order; a fixed one keeps the
+ * result deterministic), rounded once to dtype.
  *   y_perm [R,d] dtype, pair_row [R] int32, topk_gate [T,K] float32,
  *   shared_out [T,d] dtype (nullable = no shared term), y [T,d] dtype out. */
 moge_status_t moge_combine(const moge_dims_t* dims, const void* y_perm, const int32_t* pair_row,
                            const float* topk_gate, const void* shared_out, void* y,
                            void* stream);
 
-/* The whole layer forward pass on one stream with no host synchronisation:
- * scores -> softmax -> per-group top-K' -> permutation -> routed experts (each
+/* The whole layer forward pass on one stream with no host synchronisation
+ * (TechWalker page, sections 一 and 三; mokono.cn 核心亮点 1): scores -> softmax
+ * over all N experts -> per-group top-K' -> permutation -> routed experts (each
  * reads its token rows straight from x) -> shared experts -> combine.
+ * Beyond the plain layer call it takes one optional input, logits_in (route on
+ * scores the caller already has: the same fp32 scores on both sides of a parity
+ * check, or scores computed elsewhere), and returns the gates as well as the
+ * indices (topk_gate_out), so that a caller can rebuild the combine.
  *   x [T,d], w_router [N,d], router_bias [N] float32 (nullable),
  *   w_gate/w_up [N,I,d], w_down [N,d,I], ws_gate/ws_up [I_s,d], ws_down [d,I_s]
  *     (the ws_* pointers may be NULL only when shared_inter == 0),

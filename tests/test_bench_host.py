@@ -29,6 +29,9 @@ def test_algorithmic_work_of_the_decode_layer():
     assert per_token == 2 * d * N + 6 * C1.K * d * I + 6 * d * Is
     assert round(per_token / 1e6, 1) == 496.1
     assert w["active_experts"] == N
+    # the experts (S4-S6): their weights, x in and y out
+    assert w["experts"]["bytes"] == (N * 3 * d * I + 3 * d * Is + 2 * T * d) * 2
+    assert w["experts"]["flops"] == 6 * R * d * I + 6 * T * d * Is
 
 
 def test_idle_experts_read_no_weights():
