@@ -221,6 +221,29 @@ moge_status_t moge_layer_forward_packed(const moge_dims_t* dims, const void* x,
                                         float* topk_gate_out, int32_t* group_counts_out,
                                         void* ws, size_t ws_bytes, void* stream);
 
+/* moge_layer_forward_packed with no workspace argument, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The workspace is a fixed
+ * device array inside the library, MOGE_NOALLOC_SCRATCH_BYTES (128 MiB), of which
+ * every GPU that loads the library holds its own copy until the process ends.
+ * Dims whose moge_workspace_size() exceeds it give MOGE_ERR_UNSUPPORTED; at the
+ * Pangu-Pro shape (d 5120, 64 experts, K 8, width 1344, shared width 5376) that
+ * allows up to 512 tokens.  Arguments and results are those of
+ * moge_layer_forward_packed, bit for bit.  The current device must be the
+ * stream's device (MOGE_ERR_INVALID_ARG otherwise); the first call on a device
+ * looks up the array's address there.  It never allocates or frees memory.
+ * Every call on one GPU uses the same array, which keeps the last call's
+ * contents (nothing in it needs to start at zero): calls on one stream are
+ * ordered and safe, but calls that overlap in time on one GPU (several streams or
+ * threads) race and give undefined results. */
+#define MOGE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+moge_status_t moge_layer_forward_packed_noalloc(const moge_dims_t* dims, const void* x,
+                                                const void* w_router, const float* router_bias,
+                                                const void* packed, const float* logits_in,
+                                                void* y, float* logits_out,
+                                                int32_t* topk_idx_out, float* topk_gate_out,
+                                                int32_t* group_counts_out, void* stream);
+
 /* Weight-only int8 experts (W8A16).  Quantised deployment of the experts is part
  * of the inference work on the TechWalker page (section 三 推理性能优化, expert-aware
  * quantisation); the CSDN page reports W8A8 within 1.2% of full accuracy.  This is

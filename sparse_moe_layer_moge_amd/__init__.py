@@ -70,6 +70,8 @@ _SIGS = {
                                          ctypes.c_size_t, _P]),
     "moge_layer_forward_packed": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P,
                                                  _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moge_layer_forward_packed_noalloc": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P,
+                                                         _P, _P, _P, _P, _P, _P, _P]),
     "moge_w8_weights_size": (ctypes.c_size_t, [ctypes.POINTER(Dims)]),
     "moge_pack_weights_w8": (ctypes.c_int, [ctypes.POINTER(Dims)] + [_P] * 13
                              + [ctypes.c_size_t, _P]),
@@ -207,6 +209,20 @@ def layer_forward_packed(dims: Dims, x, w_router, router_bias, packed, y, ws, lo
                                          _ptr(topk_gate_out), _ptr(group_counts_out), _ptr(ws),
                                          ws.numel() * ws.element_size(), _stream(stream)),
            "moge_layer_forward_packed")
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def layer_forward_packed_noalloc(dims: Dims, x, w_router, router_bias, packed, y,
+                                 logits_in=None, logits_out=None, topk_idx_out=None,
+                                 topk_gate_out=None, group_counts_out=None, stream=None) -> None:
+    _check(lib.moge_layer_forward_packed_noalloc(ctypes.byref(dims), _ptr(x), _ptr(w_router),
+                                                 _ptr(router_bias), _ptr(packed),
+                                                 _ptr(logits_in), _ptr(y), _ptr(logits_out),
+                                                 _ptr(topk_idx_out), _ptr(topk_gate_out),
+                                                 _ptr(group_counts_out), _stream(stream)),
+           "moge_layer_forward_packed_noalloc")
 
 
 def w8_weights_size(dims: Dims) -> int:

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/moge.h"
@@ -560,6 +561,45 @@ moge_status_t layer_impl(const moge_dims_t* dims, const void* x, const void* w_r
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// The workspace of moge_layer_forward_packed_noalloc: a fixed device array, for
+// callers that cannot allocate device memory or pass a workspace.  Every GPU that
+// runs the library holds its own copy until the process ends.  In host code the
+// array's name is only a stand-in for the symbol, not a device address: its
+// address on a device comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is passed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[MOGE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (looked up on the first
+// call on each device).
+moge_status_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  CHECK(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOGE_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    CHECK(hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                    "hipGetSymbolAddress(scratch)"));
+    if (!p || reinterpret_cast<uintptr_t>(p) % 256)
+      return fail(MOGE_ERR_HIP, "scratch array of device %d at %p is not 256-byte aligned", dev,
+                  p);
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MOGE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t moge_abi_version(void) { return 1; }
@@ -767,6 +807,35 @@ moge_status_t moge_layer_forward_packed(const moge_dims_t* dims, const void* x,
   }
   return layer_impl(dims, x, w_router, router_bias, w, logits_in, y, logits_out, topk_idx_out,
                     topk_gate_out, group_counts_out, ws, ws_bytes, stream);
+}
+
+moge_status_t moge_layer_forward_packed_noalloc(const moge_dims_t* dims, const void* x,
+                                                const void* w_router, const float* router_bias,
+                                                const void* packed, const float* logits_in,
+                                                void* y, float* logits_out,
+                                                int32_t* topk_idx_out, float* topk_gate_out,
+                                                int32_t* group_counts_out, void* stream) {
+  CHECK(check_dims(dims));
+  const size_t need = make_plan(dims).total;
+  if (need > MOGE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOGE_ERR_UNSUPPORTED,
+                "these dims need %zu bytes of workspace; the fixed scratch array holds %zu "
+                "(T=%d is too large for moge_layer_forward_packed_noalloc: pass a workspace to "
+                "moge_layer_forward_packed)",
+                need, (size_t)MOGE_NOALLOC_SCRATCH_BYTES, dims->T);
+  // the scratch address is per device: the stream must belong to the current one
+  int cur = -1, sdev = -1;
+  CHECK(hip_check(hipGetDevice(&cur), "hipGetDevice"));
+  CHECK(hip_check(hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev),
+                  "hipStreamGetDevice"));
+  if (sdev != cur)
+    return fail(MOGE_ERR_INVALID_ARG,
+                "the stream belongs to device %d but device %d is current", sdev, cur);
+  void* ws = nullptr;
+  CHECK(scratch_on_current_device(&ws));
+  return moge_layer_forward_packed(dims, x, w_router, router_bias, packed, logits_in, y,
+                                   logits_out, topk_idx_out, topk_gate_out, group_counts_out, ws,
+                                   MOGE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t moge_w8_weights_size(const moge_dims_t* dims) {
