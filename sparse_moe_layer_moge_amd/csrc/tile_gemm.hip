@@ -90,8 +90,11 @@ template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false> struct Tile
   // two workgroups per CU), about the bytes in flight of the narrow rings
   static constexpr int kSmallDepth =
       W8 ? (WIDE ? 3 : kSmallW8Depth) : (WIDE ? (GATEUP ? 5 : 4) : 6);
+  // The big gate/up tile's weight stages are smaller than its activation stages
+  // (24 KiB against 32), so its weights run 3 stages ahead and fill the LDS; the
+  // weights, not the activations, were the operand its MFMAs waited for
   static constexpr int kDA = BIG ? 2 : kSmallDepth;   // activation stages in LDS
-  static constexpr int kDB = BIG ? 3 : kSmallDepth;   // weight stages in LDS
+  static constexpr int kDB = BIG ? (GATEUP ? 4 : 3) : kSmallDepth;   // weight stages in LDS
   static constexpr int kAStageBytes = kM * kLineBytes;
   // B stage: bf16 weights, kWRows / 8 fragments of 1 KiB; int8 codes, kWRows / 16
   // code tiles of 1 KiB (16 rows x 64 codes)
@@ -102,7 +105,7 @@ template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false> struct Tile
   static constexpr int kBLoads = kBStageBytes / kFragBytes / 4;
   // one load after every kEvery MFMAs
   static constexpr int kEvery = BIG ? (GATEUP ? 2 : 3) : 1;
-  static_assert(kDA <= kDB && (kDA == kDB || (kDA == 2 && kDB == 3)), "ring depths");
+  static_assert(kDA <= kDB && (kDA == kDB || (kDA == 2 && kDB >= 3)), "ring depths");
   static_assert(kWP * kWavesN == kBlocksPerTile && kTP >= 1, "wave layout");
   static_assert(kLdsBytes * kPerCU <= 160 * 1024, "LDS budget");
   static_assert((kALoads + kBLoads) * kEvery <= 4 * kTP * kWP, "loads must fit in a stage");
@@ -398,13 +401,25 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
 
   // ---- A: stage rows 8 * (kALoads * wave + i) + l / 8
   const Rsrc xr = make_rsrc(g.x, (uint64_t)g.x_rows * K * sizeof(E));
+  int a_src[S::kALoads];
+#pragma unroll
+  for (int i = 0; i < S::kALoads; ++i)
+    a_src[i] = row0 + min((wu * S::kALoads + i) * kRowsPerLoad + lr, rows - 1);
+  if (GATEUP && g.row_src) {
+    // the source rows through the permutation: every load first, then one wait
+    // (a wait per load puts several memory latencies into every tile's set-up)
+    int pair[S::kALoads];
+#pragma unroll
+    for (int i = 0; i < S::kALoads; ++i) pair[i] = g.row_src[a_src[i]];
+    const unsigned div = (unsigned)g.row_div;
+#pragma unroll
+    for (int i = 0; i < S::kALoads; ++i) a_src[i] = (int)((unsigned)pair[i] / div);
+  }
   uint32_t a_voff[S::kALoads];
 #pragma unroll
   for (int i = 0; i < S::kALoads; ++i) {
     const int r = (wu * S::kALoads + i) * kRowsPerLoad + lr;
-    const int rr = row0 + min(r, rows - 1);
-    const int src = (GATEUP && g.row_src) ? g.row_src[rr] / g.row_div : rr;
-    a_voff[i] = (uint32_t)(((size_t)src * K + kb0 * kTileK + swz_chunk(r, l & 7) * 8) * sizeof(E));
+    a_voff[i] = (uint32_t)(((size_t)a_src[i] * K + kb0 * kTileK + swz_chunk(r, l & 7) * 8) * sizeof(E));
   }
   // ---- B: the stage's weight rows in MFMA fragment order: fragment f = 2 rb + kh
   // holds rows 16 rb .. +15 and elements 32 kh .. +31 of the stage, lane j of the
@@ -567,10 +582,12 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   // the top of stage kb everything up to the last load stage kb needs has to be
   // in; what may still be outstanding is
   //   equal depths: the loads of stages kb+1 .. min(kb + kDA - 2, nk - 1);
-  //   depths 2, 3:  the B loads of stage kb + 1, if it exists.
+  //   A depth 2, B deeper: the B loads issued after A of stage kb, i.e. those of
+  //   stage kb + kDB - 2, if it exists (at kb = 0 this waits for a little more
+  //   than it must: B of stages 1 .. kDB - 3 as well).
   auto pending = [&](int kb) {
     if (S::kDA == S::kDB) return (S::kALoads + S::kBLoads) * max(0, min(S::kDA - 2, nk - 1 - kb));
-    return kb + 1 <= nk - 1 ? S::kBLoads : 0;
+    return kb + S::kDB - 2 <= nk - 1 ? S::kBLoads : 0;
   };
   constexpr int kPendSteady = S::kDA == S::kDB ? (S::kDA - 2) * (S::kALoads + S::kBLoads) : S::kBLoads;
 
