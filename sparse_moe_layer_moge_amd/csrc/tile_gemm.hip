@@ -4,14 +4,15 @@
 //
 // The TechWalker page (section 三, SwiftGMM) has the grouped matmul switch between
 // a GEMV-like and a GEMM-like mode by workload; these are the GEMM-like modes.  A
-// workgroup has 4 waves (one per SIMD) and computes one tile; there are two tile
-// shapes, chosen per expert by its row count:
+// workgroup computes one tile; there are two tile shapes, chosen per expert by its
+// row count:
 //   big   (above 128 rows): 256 rows x (96 gate/up features | 256 output columns);
-//         waves 2 (rows) x 2 (weight rows), each 128 rows x (96 | 128) weight rows
-//         as 4 x (3 | 4) blocks of 32x32 float32 accumulators.  This one is bound
-//         by the matrix cores.
+//         gate/up: 4 waves (one per SIMD), 2 (rows) x 2 (weight rows), each 128
+//         rows x 96 weight rows as 4 x 3 blocks of 32x32 float32 accumulators;
+//         down: 8 waves (two per SIMD), 2 x 4, each 128 rows x 64 columns as 4 x 2
+//         blocks.  This one is bound by the matrix cores.
 //   small (up to 128 rows): 64 rows x (64 gate/up features | 128 output columns);
-//         all four waves on the same 64 rows, each with its own 32 weight rows.
+//         4 waves, all on the same 64 rows, each with its own 32 weight rows.
 //         Wide: 64 rows x (96 features, waves 2 (rows) x 2 (weight rows) | 256
 //         columns, each wave 64 weight rows).  This one streams each expert's
 //         weights once and is bound by HBM.
@@ -29,7 +30,8 @@
 //     contiguous in the packed weight layout) per instruction.
 // The loads of later stages are spread between the MFMAs of the current one; a
 // stage boundary is a wait for the wave's own loads plus a workgroup barrier.  The
-// big tile keeps 2 activation and 3 weight stages in LDS; the small tile keeps 6 of
+// big tile keeps 2 activation and 4 (gate/up) or 3 (down) weight stages in LDS;
+// the small tile keeps 6 of
 // both (wide: 5 for gate/up, 4 for down), enough bytes in flight to cover HBM
 // latency with one workgroup per CU (on int8 codes 4 of both, 3 for the wide down
 // tile, two workgroups per CU).  An expert's last row tile is mostly partial: a
@@ -58,7 +60,12 @@ namespace moge {
 
 constexpr int kTileK = 64;              // contraction elements per stage
 constexpr int kLineBytes = kTileK * 2;  // one operand row of a stage (bf16)
-constexpr int kTileThreads = 256;       // 4 waves
+constexpr int kTileThreads = 256;       // 4 waves (one per SIMD)
+// Waves of a 256-row tile: 4 for gate/up, 8 (two per SIMD) for down.  With two
+// waves per SIMD one wave's MFMAs run while the other waits; the down tiles gained
+// about 1 % (T=4096: 0.660 -> 0.649 ms, T=16384: 2.425 -> 2.416 ms, same box), the
+// gate/up tiles, whose waves then read 43 % more from LDS per stage, lost 6 %.
+template <bool GATEUP> constexpr int big_waves() { return GATEUP ? 4 : 8; }
 constexpr int kXcds = 8;
 constexpr int kRowsPerLoad = 8;         // A rows one wave instruction moves
 constexpr int kFragBytes = 1024;        // one 16 x 32 bf16 MFMA fragment
@@ -79,8 +86,12 @@ template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false> struct Tile
   static constexpr int kM = BIG ? 256 : 64;                       // rows per tile
   static constexpr int kWRows = (BIG || WIDE) ? (GATEUP ? 192 : 256) : 128;  // weight rows per tile
   static constexpr int kFeat = kWRows / 2;                         // gate/up features per tile
-  static constexpr int kWavesM = (BIG || (WIDE && GATEUP)) ? 2 : 1;  // waves along the rows
-  static constexpr int kWavesN = 4 / kWavesM;
+  static constexpr int kWaves = BIG ? big_waves<GATEUP>() : 4;
+  static constexpr int kThreads = kWaves * 64;
+  // waves along the rows
+  static constexpr int kWavesM =
+      BIG ? (kWaves == 8 ? (GATEUP ? 4 : 2) : 2) : ((WIDE && GATEUP) ? 2 : 1);
+  static constexpr int kWavesN = kWaves / kWavesM;
   static constexpr int kTP = kM / kWavesM / 32;                    // 32-row blocks per wave
   static constexpr int kBlocksPerTile = kWRows / 32;               // 32-row weight blocks
   static constexpr int kWP = kBlocksPerTile / kWavesN;             // ... per wave
@@ -101,10 +112,12 @@ template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false> struct Tile
   static constexpr int kBStageBytes = kWRows * kTileK * (W8 ? 1 : 2);
   static constexpr int kLdsBytes = kDA * kAStageBytes + kDB * kBStageBytes;
   // wave instructions per stage: A (8 rows each), B (one fragment each)
-  static constexpr int kALoads = kM / kRowsPerLoad / 4;
-  static constexpr int kBLoads = kBStageBytes / kFragBytes / 4;
+  static constexpr int kALoads = kM / kRowsPerLoad / kWaves;
+  static constexpr int kBLoads = kBStageBytes / kFragBytes / kWaves;
   // one load after every kEvery MFMAs
-  static constexpr int kEvery = BIG ? (GATEUP ? 2 : 3) : 1;
+  static constexpr int kEvery = BIG ? 3 : 1;
+  static_assert(kALoads * kWaves * kRowsPerLoad == kM &&
+                kBLoads * kWaves * kFragBytes == kBStageBytes, "loads cover a stage");
   static_assert(kDA <= kDB && (kDA == kDB || (kDA == 2 && kDB >= 3)), "ring depths");
   static_assert(kWP * kWavesN == kBlocksPerTile && kTP >= 1, "wave layout");
   static_assert(kLdsBytes * kPerCU <= 160 * 1024, "LDS budget");
@@ -278,7 +291,7 @@ __device__ __forceinline__ bool seg_lanes_find(const SegLanes& t, int mt, int* e
 // writes float32 partial sums (a separate instantiation, so that the plain big
 // kernels keep their registers).  The small shape handles both at run time.
 template <bool GATEUP, bool BIG, bool W8, bool SPLIT = false, bool WIDE = false>
-__global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
+__global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
   typedef bf16 E;
   typedef TileShape<GATEUP, BIG, W8, WIDE> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::kLdsBytes];
@@ -722,7 +735,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg
   __syncthreads();
   const int ld = GATEUP ? g.inter : d;
   const int col0 = nt * kOutCols;
-  for (int i = tid; i < rows * kNC; i += kTileThreads) {
+  for (int i = tid; i < rows * kNC; i += S::kThreads) {
     const int r = i / kNC, c = i - r * kNC;
     const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * kPitch + ((c ^ (r & (kNCp - 1))) << 4));
     *reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * ld + col0 + c * 8) = v;
@@ -793,7 +806,7 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
   }
   const long long grid = per_xcd * kXcds;
   if (grid > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8, SPLIT, WIDE>), dim3((unsigned)grid), dim3(kTileThreads),
+  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8, SPLIT, WIDE>), dim3((unsigned)grid), dim3(S::kThreads),
                      0, st, a, bb, d);
   return hipGetLastError();
 }
