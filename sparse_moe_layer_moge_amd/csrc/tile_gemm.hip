@@ -287,52 +287,47 @@ __device__ __forceinline__ bool seg_lanes_find(const SegLanes& t, int mt, int* e
   return true;
 }
 
-// SPLIT (big shape only): every tile computes one slice of the contraction and
-// writes float32 partial sums (a separate instantiation, so that the plain big
-// kernels keep their registers).  The small shape handles both at run time.
-template <bool GATEUP, bool BIG, bool W8, bool SPLIT = false, bool WIDE = false>
-__global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
-  typedef bf16 E;
+// The tile list of up to two segments on one tile shape (see the file comment).
+// Every wave holds the totals (init); wave 0 picks the tile of list entry `it` of
+// XCD `x` (select) and leaves its descriptor in `s_tile`: segment (-1: none),
+// expert, first row, rows, weight tile, contraction slice.
+template <bool GATEUP, bool BIG, bool W8, bool SPLIT, bool WIDE>
+struct TileList {
   typedef TileShape<GATEUP, BIG, W8, WIDE> S;
-  __shared__ __attribute__((aligned(1024))) char lds[S::kLdsBytes];
-  char* const ldsA = lds;
-  char* const ldsB = lds + S::kDA * S::kAStageBytes;
-  // the tile descriptor lives in the last weight buffer, which the loads issued
-  // before the main loop leave alone and later loads overwrite only after the
-  // main loop's first barrier
-  int* s_tile = reinterpret_cast<int*>(ldsB + (S::kDB - 1) * S::kBStageBytes);
-
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63;
-  // ---- the tile lists (every wave computes the totals) -----------------------
-  // entries per row tile: weight tiles times contraction slices (slice-major)
-  constexpr bool kSliced = !BIG || SPLIT;   // this instantiation handles slices
-  const int nta = (GATEUP ? a.inter / S::kFeat : d / S::kWRows) * (kSliced ? a.ksplit : 1);
-  const int ntb = b.n_exp ? (GATEUP ? b.inter / S::kFeat : d / S::kWRows) * (kSliced ? b.ksplit : 1) : 0;
-  // segments of at most 64 experts: per-lane tables (one round of loads for
-  // both); larger ones are scanned again for every tile
-  const bool lanes = a.n_exp <= 64 && b.n_exp <= 64;
+  static constexpr bool kSliced = !BIG || SPLIT;   // this instantiation handles slices
+  int nta = 0, ntb = 0, ma = 0, mb = 0, tot0 = 0, tot1 = 0, ch0 = 0, ch1 = 0;
+  bool lanes = false, b_first = false;
   SegLanes la, lb;
-  int ma = 0, mb = 0;
-  if (lanes) {
-    la = seg_lanes<S::kM>(a, &ma);
-    if (b.n_exp) lb = seg_lanes<S::kM>(b, &mb);
-  } else {
-    ma = seg_total_tiles<S::kM>(a);
-    mb = b.n_exp ? seg_total_tiles<S::kM>(b) : 0;
+
+  __device__ __forceinline__ void init(const TileSeg& a, const TileSeg& b, int d) {
+    // entries per row tile: weight tiles times contraction slices (slice-major)
+    nta = a.n_exp ? (GATEUP ? a.inter / S::kFeat : d / S::kWRows) * (kSliced ? a.ksplit : 1) : 0;
+    ntb = b.n_exp ? (GATEUP ? b.inter / S::kFeat : d / S::kWRows) * (kSliced ? b.ksplit : 1) : 0;
+    // segments of at most 64 experts: per-lane tables (one round of loads for
+    // both); larger ones are scanned again for every tile
+    lanes = a.n_exp <= 64 && b.n_exp <= 64;
+    if (lanes) {
+      if (a.n_exp) la = seg_lanes<S::kM>(a, &ma);
+      if (b.n_exp) lb = seg_lanes<S::kM>(b, &mb);
+    } else {
+      ma = a.n_exp ? seg_total_tiles<S::kM>(a) : 0;
+      mb = b.n_exp ? seg_total_tiles<S::kM>(b) : 0;
+    }
+    // every XCD takes an equal share of each segment; the segment with the longer
+    // contraction (more work per tile) goes first, so its tiles do not pile up at
+    // the end
+    b_first = (GATEUP ? d : b.inter) > (GATEUP ? d : a.inter);
+    tot0 = b_first ? mb * ntb : ma * nta;
+    tot1 = b_first ? ma * nta : mb * ntb;
+    ch0 = (tot0 + kXcds - 1) / kXcds;
+    ch1 = (tot1 + kXcds - 1) / kXcds;
   }
-  // every XCD takes an equal share of each segment; the segment with the longer
-  // contraction (more work per tile) goes first, so its tiles do not pile up at
-  // the end
-  const bool b_first = (GATEUP ? d : b.inter) > (GATEUP ? d : a.inter);
-  const int tot0 = b_first ? mb * ntb : ma * nta, tot1 = b_first ? ma * nta : mb * ntb;
-  const int ch0 = (tot0 + kXcds - 1) / kXcds, ch1 = (tot1 + kXcds - 1) / kXcds;
-  // workgroup b runs on XCD b % 8 and takes that XCD's entry b / 8; the small shape
-  // (launched with as many workgroups as fit the CUs) walks on to b / 8 + G, b / 8 + 2G,
-  // ... (G workgroups per XCD), so the CUs of an XCD work on neighbouring entries
-  const int x = blockIdx.x % kXcds;
-  auto run_tile = [&](int it) {
-  if (w == 0) {
+  // list entries of one XCD
+  __device__ __forceinline__ int entries() const { return ch0 + ch1; }
+
+  __device__ __forceinline__ void select(const TileSeg& a, const TileSeg& b, int it, int x,
+                                         int* s_tile) const {
+    const int l = threadIdx.x & 63;
     int seg = -1, e = 0, row0 = 0, rows = 0, nt = 0, ks = 0;
     int which = -1, t = 0;
     if (it < ch0) {
@@ -392,14 +387,19 @@ __global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) v
       s_tile[5] = ks;
     }
   }
-  __syncthreads();
-  const int seg = s_tile[0];
-  if (seg >= 0) {
-  const TileSeg g = seg == 0 ? a : b;
-  const int e = s_tile[1];
-  const int row0 = s_tile[2], rows = s_tile[3];
-  const int nt = s_tile[4];
-  const int kslice = kSliced ? s_tile[5] : 0;
+};
+
+// One tile: load, multiply and write it (every wave of the workgroup).
+template <bool GATEUP, bool BIG, bool W8, bool SPLIT, bool WIDE>
+__device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d, int e, int row0,
+                                             int rows, int nt, int kslice) {
+  typedef bf16 E;
+  typedef TileShape<GATEUP, BIG, W8, WIDE> S;
+  constexpr bool kSliced = !BIG || SPLIT;
+  char* const ldsA = lds;
+  char* const ldsB = lds + S::kDA * S::kAStageBytes;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63;
   const int K = GATEUP ? d : g.inter;              // contraction length of this segment
   const int nk = K / kTileK / (kSliced ? g.ksplit : 1);  // stages of this tile's slice
   const int kb0 = kslice * nk;                     // its first stage
@@ -741,21 +741,48 @@ __global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) v
     *reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * ld + col0 + c * 8) = v;
   }
   }  // ksplit
-  }  // seg >= 0
+}
+
+// SPLIT (big shape only): every tile computes one slice of the contraction and
+// writes float32 partial sums (a separate instantiation, so that the plain big
+// kernels keep their registers).  The small shape handles both at run time.
+template <bool GATEUP, bool BIG, bool W8, bool SPLIT = false, bool WIDE = false>
+__global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
+  typedef TileShape<GATEUP, BIG, W8, WIDE> S;
+  __shared__ __attribute__((aligned(1024))) char lds[S::kLdsBytes];
+  // the tile descriptor lives in the last weight buffer, which the loads issued
+  // before the main loop leave alone and later loads overwrite only after the
+  // main loop's first barrier
+  int* s_tile = reinterpret_cast<int*>(lds + S::kDA * S::kAStageBytes + (S::kDB - 1) * S::kBStageBytes);
+  TileList<GATEUP, BIG, W8, SPLIT, WIDE> list;
+  list.init(a, b, d);
+  // workgroup b runs on XCD b % 8 and takes that XCD's entry b / 8; the small shape
+  // (launched with as many workgroups as fit the CUs) walks on to b / 8 + G, b / 8 + 2G,
+  // ... (G workgroups per XCD), so the CUs of an XCD work on neighbouring entries
+  const int x = blockIdx.x % kXcds;
+  auto run_tile = [&](int it) {
+    if ((threadIdx.x >> 6) == 0) list.select(a, b, it, x, s_tile);
+    __syncthreads();
+    const int seg = s_tile[0];
+    if (seg >= 0)
+      tile_compute<GATEUP, BIG, W8, SPLIT, WIDE>(lds, seg == 0 ? a : b, d, s_tile[1], s_tile[2],
+                                                 s_tile[3], s_tile[4],
+                                                 decltype(list)::kSliced ? s_tile[5] : 0);
   };
   if constexpr (BIG) {
     // one tile per workgroup: the big shape's registers are nearly all taken by the
     // accumulators, and nothing may stay live across tiles
-    if ((int)(blockIdx.x / kXcds) < ch0 + ch1) run_tile(blockIdx.x / kXcds);
+    if ((int)(blockIdx.x / kXcds) < list.entries()) run_tile(blockIdx.x / kXcds);
   } else {
     const int gx = gridDim.x / kXcds;
-    for (int it = blockIdx.x / kXcds; it < ch0 + ch1; it += gx) {
+    for (int it = blockIdx.x / kXcds; it < list.entries(); it += gx) {
       run_tile(it);
       // every wave is done with this tile's LDS (and the descriptor) before the next
       __syncthreads();
     }
   }
 }
+
 
 int small_down_cols(bool wide) {
   return wide ? TileShape<false, false, false, true>::kWRows : TileShape<false, false>::kWRows;
