@@ -140,6 +140,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Inclusive prefix sum of an int over the 64 lanes with DPP moves, which stay in
+// the vector unit (a shuffle is an LDS permute with a round trip each): shifts by
+// 1, 2, 4 and 8 lanes inside every row of 16 lanes, then lane 15 added to row 1
+// and 3 and lane 31 to rows 2 and 3.  Lanes with no source lane add 0.
+__device__ __forceinline__ int wave_scan_add(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+// lane `src` (wave-uniform) of v
+__device__ __forceinline__ int lane_value(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int l = threadIdx.x & (kWave - 1);
   return l == 0 ? 0ull : (~0ull >> (64 - l));

@@ -78,15 +78,7 @@ __device__ __forceinline__ void chunk_scatter(const int32_t* __restrict__ idx, i
 }
 
 // inclusive prefix sum across the 64 lanes of a wave
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (l >= o) v += u;
-  }
-  return v;
-}
+__device__ __forceinline__ int wave_incl_scan(int v) { return wave_scan_add(v); }
 
 // offsets[e] = exclusive prefix of counts over experts (N <= 256, one wave: lane l
 // owns experts 4l .. 4l+3); the total lands in off[N]

@@ -217,25 +217,20 @@ __device__ __forceinline__ bool seg_find_expert(const TileSeg& g, int mt, int* e
     int lo = 0, cnt = 0;
     const int nt = e < g.n_exp ? seg_expert_tiles<kM>(g, e, &lo, &cnt) : 0;
     // inclusive prefix of nt across the wave
-    int inc = nt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(inc, o, 64);
-      if (l >= o) inc += v;
-    }
+    const int inc = wave_scan_add(nt);
     const int start = base + inc - nt;
     const bool mine = nt > 0 && mt >= start && mt < start + nt;
     const uint64_t m = __ballot(mine);
     if (m) {
       const int src = __ffsll((long long)m) - 1;
-      *e_out = __shfl(e, src, 64);
-      *first_out = __shfl(start, src, 64);
-      *lo_out = __shfl(lo, src, 64);
-      *cnt_out = __shfl(cnt, src, 64);
-      *nrt_out = __shfl(nt, src, 64);
+      *e_out = lane_value(e, src);
+      *first_out = lane_value(start, src);
+      *lo_out = lane_value(lo, src);
+      *cnt_out = lane_value(cnt, src);
+      *nrt_out = lane_value(nt, src);
       return true;
     }
-    base += __shfl(inc, 63, 64);
+    base += lane_value(inc, 63);
   }
   return false;
 }
@@ -247,9 +242,7 @@ template <int kM> __device__ __forceinline__ int seg_total_tiles(const TileSeg& 
     int lo, cnt;
     s += seg_expert_tiles<kM>(g, e, &lo, &cnt);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-  return s;
+  return lane_value(wave_scan_add(s), 63);
 }
 
 // A segment of at most 64 experts held across the lanes of a wave: lane e has
@@ -263,14 +256,9 @@ template <int kM> __device__ __forceinline__ SegLanes seg_lanes(const TileSeg& g
   const int l = threadIdx.x & 63;
   SegLanes t;
   if (l < g.n_exp) t.nt = seg_expert_tiles<kM>(g, l, &t.lo, &t.cnt);
-  int inc = t.nt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(inc, o, 64);
-    if (l >= o) inc += v;
-  }
+  const int inc = wave_scan_add(t.nt);
   t.start = inc - t.nt;
-  *total = __shfl(inc, 63, 64);
+  *total = lane_value(inc, 63);
   return t;
 }
 // The expert that owns row tile `mt` (as seg_find_expert, from the lanes)
@@ -280,10 +268,10 @@ __device__ __forceinline__ bool seg_lanes_find(const SegLanes& t, int mt, int* e
   if (!m) return false;
   const int src = __ffsll((long long)m) - 1;
   *e_out = src;
-  *first_out = __shfl(t.start, src, 64);
-  *lo_out = __shfl(t.lo, src, 64);
-  *cnt_out = __shfl(t.cnt, src, 64);
-  *nrt_out = __shfl(t.nt, src, 64);
+  *first_out = lane_value(t.start, src);
+  *lo_out = lane_value(t.lo, src);
+  *cnt_out = lane_value(t.cnt, src);
+  *nrt_out = lane_value(t.nt, src);
   return true;
 }
 
