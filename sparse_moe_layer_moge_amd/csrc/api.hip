@@ -122,7 +122,7 @@ moge_status_t check_w8_dims(const moge_dims_t* d) {
 // ---------------------------------------------------------------------------
 struct Plan {
   size_t partial, idx, gate, blk_cnt, blk_base, counts, offsets, gcounts, sorted_pair, pair_row,
-      h, hs, y_perm, sh, sh_part, total;
+      h, hs, y_perm, sh, sh_part, sched, total;
   int ksplit;
 };
 
@@ -160,6 +160,39 @@ bool wide_gateup(long long R, int N, int inter, int shared_inter) {
   return many_small_tiles(R, N) && inter % f == 0 && shared_inter % f == 0;
 }
 
+// Row ranges of the routed experts: the streaming kernels take experts with at
+// most `stream_max` rows, the 64-row tiles those up to `small_max`, the 256-row
+// tiles the rest.  Each expert's kernel is chosen on the device from its row
+// count, and the host cannot see the counts, so every range gets a launch, and a
+// launch that finds no expert still costs about 4 us.  The mean rows per expert
+// (R / N) is known on the host; a range that is unlikely to hold an expert at that
+// mean joins its neighbour (any kernel handles any row count):
+//   mean >= 1.5 * kStreamMaxRows:    experts of up to kStreamMaxRows rows take the
+//                                    64-row tiles (no streaming launch);
+//   mean <= kSmallTileMaxRows / 2:   experts above kSmallTileMaxRows rows stay on
+//                                    64-row tiles (no 256-row launch);
+//   mean >= 2 * kSmallTileMaxRows:   every routed expert takes 256-row tiles.
+struct RoutedRanges {
+  int stream_max, small_max;
+};
+RoutedRanges routed_ranges(long long R, int N, bool big_tiles) {
+  RoutedRanges r{moge::kStreamMaxRows, big_tiles ? moge::kSmallTileMaxRows : INT_MAX};
+  const double mean = N > 0 ? (double)R / N : 0.0;
+  if (mean >= 1.5 * moge::kStreamMaxRows) r.stream_max = 0;
+  if (big_tiles && mean <= moge::kSmallTileMaxRows / 2) r.small_max = INT_MAX;
+  if (big_tiles && mean >= 2.0 * moge::kSmallTileMaxRows) r.stream_max = r.small_max = 0;
+  return r;
+}
+
+// The launches that mix tile shapes (routed experts on 64-row tiles beside the
+// shared segment on 256-row tiles, moge::launch_ffn_mixed) serve batches whose
+// routed experts all take 64-row tiles and whose shared segment is above the
+// 64-row tiles' limit in both projections: a mean of 48 to 64 rows per expert.
+bool mixed_regime(bool tiles_ok, const RoutedRanges& rr, int shared_rows) {
+  return tiles_ok && rr.stream_max == 0 && rr.small_max == INT_MAX &&
+         shared_rows > moge::kSharedSmallGateUpRows && shared_rows > moge::kSharedSmallDownRows;
+}
+
 // w8: the int8 layer, whose shared segment takes 64-row tiles at every size above
 // the streaming limit
 SharedSplit shared_split(const moge_dims_t* d, bool w8) {
@@ -171,6 +204,8 @@ SharedSplit shared_split(const moge_dims_t* d, bool w8) {
   // (down) per tile, narrow or wide as the launch will be; 256-row tiles: 96
   // features or 256 columns
   const long long R = (long long)T * d->M * d->k_per_group;
+  // the bf16 layer's mixed launches run the shared segment unsplit
+  if (!w8 && mixed_regime(true, routed_ranges(R, d->N, true), T)) return s;
   if (w8 || T <= moge::kSharedSmallGateUpRows)
     s.gu = moge::tile_ksplit(
         T, d->d, Is / moge::small_gateup_feats(!w8 && wide_gateup(R, d->N, d->inter, Is)), 64);
@@ -222,6 +257,7 @@ Plan make_plan(const moge_dims_t* d) {
   const size_t part_bf16 = split_part_bytes(d, shared_split(d, false));
   const size_t part_w8 = d->dtype == MOGE_BF16 ? split_part_bytes(d, shared_split(d, true)) : 0;
   p.sh_part = take(part_bf16 > part_w8 ? part_bf16 : part_w8);
+  p.sched = take(moge::kSchedInts * 4);
   p.total = o;
   return p;
 }
@@ -273,30 +309,6 @@ moge::TileSeg tile_view(const moge::FfnSeg& f, bool gateup) {
   return t;
 }
 
-// Row ranges of the routed experts: the streaming kernels take experts with at
-// most `stream_max` rows, the 64-row tiles those up to `small_max`, the 256-row
-// tiles the rest.  Each expert's kernel is chosen on the device from its row
-// count, and the host cannot see the counts, so every range gets a launch, and a
-// launch that finds no expert still costs about 4 us.  The mean rows per expert
-// (R / N) is known on the host; a range that is unlikely to hold an expert at that
-// mean joins its neighbour (any kernel handles any row count):
-//   mean >= 1.5 * kStreamMaxRows:    experts of up to kStreamMaxRows rows take the
-//                                    64-row tiles (no streaming launch);
-//   mean <= kSmallTileMaxRows / 2:   experts above kSmallTileMaxRows rows stay on
-//                                    64-row tiles (no 256-row launch);
-//   mean >= 2 * kSmallTileMaxRows:   every routed expert takes 256-row tiles.
-struct RoutedRanges {
-  int stream_max, small_max;
-};
-RoutedRanges routed_ranges(long long R, int N, bool big_tiles) {
-  RoutedRanges r{moge::kStreamMaxRows, big_tiles ? moge::kSmallTileMaxRows : INT_MAX};
-  const double mean = N > 0 ? (double)R / N : 0.0;
-  if (mean >= 1.5 * moge::kStreamMaxRows) r.stream_max = 0;
-  if (big_tiles && mean <= moge::kSmallTileMaxRows / 2) r.small_max = INT_MAX;
-  if (big_tiles && mean >= 2.0 * moge::kSmallTileMaxRows) r.stream_max = r.small_max = 0;
-  return r;
-}
-
 // Both projections of up to two segments.  The routed experts go to the streaming,
 // 64-row and 256-row kernels by the ranges routed_ranges gives; the shared segment
 // has its own limits (kSharedStreamMaxRows, kSharedSmallGateUpRows,
@@ -306,7 +318,7 @@ RoutedRanges routed_ranges(long long R, int N, bool big_tiles) {
 // the float32 partial-sum region (used when a slice count is above 1).
 moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh,
                       hipStream_t st, bool marks, SharedSplit split = SharedSplit{},
-                      float* sh_part = nullptr) {
+                      float* sh_part = nullptr, int* sched = nullptr) {
   // the tile path covers bf16 and its tile shapes; everything else streams
   const bool tiles_ok = dtype == MOGE_BF16 && moge::tile_path_ok(d, routed.inter) &&
                         (!sh || moge::tile_path_ok(d, sh->inter));
@@ -326,6 +338,11 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
   // tile launches: routed experts with lo < rows <= hi, the shared segment with
   // sh_lo < rows <= sh_hi
   struct Range { int lo, hi, sh_lo, sh_hi; bool big; };
+  // a batch whose routed experts all take 64-row tiles (none streams, none takes
+  // 256-row tiles) while the shared segment takes 256-row tiles in both
+  // projections: one launch per projection for both, with the shared
+  // contraction unsplit (the routed tiles fill the CUs beside it)
+  const bool mixed = sched && mixed_regime(tiles_ok, rr, sh ? sh->rows : 0);
   for (int gateup = 1; gateup >= 0; --gateup) {
     const int sh_big = gateup ? moge::kSharedSmallGateUpRows : moge::kSharedSmallDownRows;
     const Range ranges[2] = {{thr, thr_big, sh_thr, sh_big, false},
@@ -336,6 +353,19 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
     else if (stream_launch)
       CHECK(hip_check(moge::launch_ffn_down(dtype, d, rs, sh_stream ? sh : nullptr, st),
                       "expert down"));
+    if (mixed) {
+      moge::TileSeg a = tile_view(routed, gateup);
+      a.thr = 0;
+      a.thr_hi = INT_MAX;
+      moge::TileSeg b = tile_view(*sh, gateup);
+      b.thr = 0;
+      b.thr_hi = INT_MAX;
+      CHECK(hip_check(moge::launch_ffn_mixed(gateup, d, a, b, gateup ? wide_gu : wide_dn, sched, st),
+                      gateup ? "expert gate/up tiles (routed and shared)"
+                             : "expert down tiles (routed and shared)"));
+      if (marks) mark(gateup ? 4 : 5, st);
+      continue;
+    }
     for (const Range& rg : ranges) {
       const bool routed_here = tiles_ok && T > rg.lo && rg.lo < rg.hi;
       const bool sh_here = tiles_ok && sh && sh->rows > rg.sh_lo && sh->rows <= rg.sh_hi;
@@ -546,7 +576,7 @@ moge_status_t layer_impl(const moge_dims_t* dims, const void* x, const void* w_r
     CHECK(run_ffn_w8(dims->d, T, routed, shared ? &sh : nullptr, st, true, split, sh_part));
   else
     CHECK(run_ffn(dims->dtype, dims->d, T, routed, shared ? &sh : nullptr, st, true, split,
-                  sh_part));
+                  sh_part, at<int>(ws, p.sched)));
   // S7 combine (the shared term as the slices' partial sums when its down
   // projection was split)
   const bool dn_parts = shared && split.dn > 1;

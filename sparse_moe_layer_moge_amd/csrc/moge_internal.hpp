@@ -141,6 +141,13 @@ struct TileSeg {
 // needing a width divisible by 96, or 256-column down tiles, needing d % 256 == 0)
 hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const TileSeg* b,
                            hipStream_t st, bool wide = false);
+// one projection (gate/up or down) of the routed experts on 64-row tiles (narrow
+// or wide) and of one unsplit shared segment on 256-row tiles, in one launch;
+// sched: kSchedInts ints of device memory the launch zeroes and uses as the XCDs'
+// work counters
+constexpr int kSchedInts = 16 * 8;
+hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const TileSeg& big,
+                            bool wide, int* sched, hipStream_t st);
 // shapes the tile kernels cover (96-feature gate/up tiles, 256-column down tiles)
 bool tile_path_ok(int d, int inter);
 // 64-row tiles on int8 codes (tiles from `thr` rows up), and the shapes they cover

@@ -82,11 +82,13 @@ constexpr int kSmallW8Depth = 4;
 // down 0.245 -> 0.218 ms and gate/up 0.381 -> 0.367 ms, int8 down 0.156 ->
 // 0.144 ms); a launch of one round (the split shared segment of a small batch)
 // keeps more, narrower tiles.
-template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false> struct TileShape {
+// WAVES: 0 for the shape's own wave count, 4 to force one wave per SIMD (a big
+// tile in a launch whose other tiles run 4 waves)
+template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false, int WAVES = 0> struct TileShape {
   static constexpr int kM = BIG ? 256 : 64;                       // rows per tile
   static constexpr int kWRows = (BIG || WIDE) ? (GATEUP ? 192 : 256) : 128;  // weight rows per tile
   static constexpr int kFeat = kWRows / 2;                         // gate/up features per tile
-  static constexpr int kWaves = BIG ? big_waves<GATEUP>() : 4;
+  static constexpr int kWaves = WAVES ? WAVES : (BIG ? big_waves<GATEUP>() : 4);
   static constexpr int kThreads = kWaves * 64;
   // waves along the rows
   static constexpr int kWavesM =
@@ -279,9 +281,9 @@ __device__ __forceinline__ bool seg_lanes_find(const SegLanes& t, int mt, int* e
 // Every wave holds the totals (init); wave 0 picks the tile of list entry `it` of
 // XCD `x` (select) and leaves its descriptor in `s_tile`: segment (-1: none),
 // expert, first row, rows, weight tile, contraction slice.
-template <bool GATEUP, bool BIG, bool W8, bool SPLIT, bool WIDE>
+template <bool GATEUP, bool BIG, bool W8, bool SPLIT, bool WIDE, int WAVES = 0>
 struct TileList {
-  typedef TileShape<GATEUP, BIG, W8, WIDE> S;
+  typedef TileShape<GATEUP, BIG, W8, WIDE, WAVES> S;
   static constexpr bool kSliced = !BIG || SPLIT;   // this instantiation handles slices
   int nta = 0, ntb = 0, ma = 0, mb = 0, tot0 = 0, tot1 = 0, ch0 = 0, ch1 = 0;
   bool lanes = false, b_first = false;
@@ -378,11 +380,11 @@ struct TileList {
 };
 
 // One tile: load, multiply and write it (every wave of the workgroup).
-template <bool GATEUP, bool BIG, bool W8, bool SPLIT, bool WIDE>
+template <bool GATEUP, bool BIG, bool W8, bool SPLIT, bool WIDE, int WAVES = 0>
 __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d, int e, int row0,
                                              int rows, int nt, int kslice) {
   typedef bf16 E;
-  typedef TileShape<GATEUP, BIG, W8, WIDE> S;
+  typedef TileShape<GATEUP, BIG, W8, WIDE, WAVES> S;
   constexpr bool kSliced = !BIG || SPLIT;
   char* const ldsA = lds;
   char* const ldsB = lds + S::kDA * S::kAStageBytes;
@@ -772,6 +774,70 @@ __global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) v
 }
 
 
+__global__ void k_zero_i32(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// Both projections of a decode batch of a few hundred tokens: the routed experts
+// (a few dozen rows each) on 64-row tiles and the shared segment (every token) on
+// 256-row tiles, in one launch per projection.  The shared tiles are bound by the
+// matrix cores and the routed ones by HBM; side by side they keep both busy, where
+// launches of their own leave the matrix cores idle during the routed one and
+// HBM during the shared one.  A shared tile takes about as long as a few routed
+// ones, so a fixed share of list entries per workgroup would leave the workgroups
+// that drew one behind the rest: the workgroups of an XCD instead take the
+// entries of that XCD's list (shared tiles first) one at a time from a counter of
+// their own, so neighbouring entries still run side by side there.  `sched` holds
+// the 8 counters, 16 ints apart, zero at launch.  The shared tiles run 4 waves
+// here, as the routed ones do.
+template <bool GATEUP, bool WIDE>
+__global__ __launch_bounds__(kTileThreads, 1) void k_ffn_mixed(TileSeg small, TileSeg big, int d,
+                                                               int* sched) {
+  typedef TileShape<GATEUP, false, false, WIDE> SS;
+  typedef TileShape<GATEUP, true, false, false, 4> SB;
+  static_assert(SS::kThreads == kTileThreads && SB::kThreads == kTileThreads,
+                "both tile shapes run 4 waves");
+  constexpr int kLds = SS::kLdsBytes > SB::kLdsBytes ? SS::kLdsBytes : SB::kLdsBytes;
+  __shared__ __attribute__((aligned(1024))) char lds[kLds];
+  // each shape's descriptor in its own last weight buffer (see k_ffn_tile); the
+  // entry a workgroup took beside the big shape's
+  int* s_small = reinterpret_cast<int*>(lds + SS::kDA * SS::kAStageBytes + (SS::kDB - 1) * SS::kBStageBytes);
+  int* s_big = reinterpret_cast<int*>(lds + SB::kDA * SB::kAStageBytes + (SB::kDB - 1) * SB::kBStageBytes);
+  int* s_it = s_big + 8;
+  const TileSeg none{};
+  TileList<GATEUP, false, false, false, WIDE> ls;
+  ls.init(small, none, d);
+  TileList<GATEUP, true, false, false, false, 4> lb;
+  lb.init(big, none, d);
+  const int x = blockIdx.x % kXcds;
+  const int nb = lb.entries(), n = nb + ls.entries();
+  for (;;) {
+    if (threadIdx.x == 0)
+      *s_it = __hip_atomic_fetch_add(sched + 16 * x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int it = *s_it;
+    if (it >= n) break;   // every workgroup reaches this: the counter only grows
+    const bool is_big = it < nb;
+    if ((threadIdx.x >> 6) == 0) {
+      if (is_big)
+        lb.select(big, none, it, x, s_big);
+      else
+        ls.select(small, none, it - nb, x, s_small);
+    }
+    __syncthreads();
+    const int* t = is_big ? s_big : s_small;
+    if (t[0] >= 0) {
+      if (is_big)
+        tile_compute<GATEUP, true, false, false, false, 4>(lds, big, d, t[1], t[2], t[3], t[4], 0);
+      else
+        tile_compute<GATEUP, false, false, false, WIDE>(lds, small, d, t[1], t[2], t[3], t[4], t[5]);
+    }
+    // every wave is done with this tile's LDS (and the descriptors) before the next
+    __syncthreads();
+  }
+}
+
 int small_down_cols(bool wide) {
   return wide ? TileShape<false, false, false, true>::kWRows : TileShape<false, false>::kWRows;
 }
@@ -823,6 +889,39 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
   if (grid > INT_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8, SPLIT, WIDE>), dim3((unsigned)grid), dim3(S::kThreads),
                      0, st, a, bb, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const TileSeg& big,
+                            bool wide, int* sched, hipStream_t st) {
+  if (big.ksplit != 1 || small.ksplit != 1 || !sched) return hipErrorInvalidValue;
+  long long per_xcd;
+  if (gateup) {
+    typedef TileShape<true, true, false, false, 4> SB;
+    const int fs = wide ? TileShape<true, false, false, true>::kFeat : TileShape<true, false>::kFeat;
+    if (big.inter % SB::kFeat || small.inter % fs) return hipErrorInvalidValue;
+    per_xcd = (tile_bound(big, SB::kM) * (big.inter / SB::kFeat) + kXcds - 1) / kXcds +
+              (tile_bound(small, 64) * (small.inter / fs) + kXcds - 1) / kXcds;
+  } else {
+    typedef TileShape<false, true, false, false, 4> SB;
+    const int cs = small_down_cols(wide);
+    if (d % SB::kWRows || d % cs) return hipErrorInvalidValue;
+    per_xcd = (tile_bound(big, SB::kM) * (d / SB::kWRows) + kXcds - 1) / kXcds +
+              (tile_bound(small, 64) * (d / cs) + kXcds - 1) / kXcds;
+  }
+  if (per_xcd == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(kSchedInts), 0, st, sched, kSchedInts);
+  const long long slots = device_cus() / kXcds;
+  const long long grid = (per_xcd < slots ? per_xcd : (slots > 0 ? slots : 1)) * kXcds;
+  const dim3 g((unsigned)grid), b(kTileThreads);
+  if (gateup && wide)
+    hipLaunchKernelGGL((k_ffn_mixed<true, true>), g, b, 0, st, small, big, d, sched);
+  else if (gateup)
+    hipLaunchKernelGGL((k_ffn_mixed<true, false>), g, b, 0, st, small, big, d, sched);
+  else if (wide)
+    hipLaunchKernelGGL((k_ffn_mixed<false, true>), g, b, 0, st, small, big, d, sched);
+  else
+    hipLaunchKernelGGL((k_ffn_mixed<false, false>), g, b, 0, st, small, big, d, sched);
   return hipGetLastError();
 }
 

@@ -564,8 +564,11 @@ def test_layer_one_expert_per_group_takes_everything(lib, name, T):
     assert normwise_rel_err(values(out["y"])[tok], ref["y"]) <= tolerance(cfg)
 
 
+# split_shared: the layer splits the shared experts' contraction (a 64-token batch);
+# at 456 tokens the shared segment runs unsplit beside the routed tiles, so the
+# layer equals the step path bit for bit there
 @pytest.mark.parametrize("name,T,split_shared", [("C0", 64, False), ("C1", 64, True),
-                                                 ("C1", 17, False), ("C2", 456, True)])
+                                                 ("C1", 17, False), ("C2", 456, False)])
 def test_layer_deterministic_and_equal_to_step_path(lib, name, T, split_shared):
     import torch
     cfg = CONFIGS[name]
