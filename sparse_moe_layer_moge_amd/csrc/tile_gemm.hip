@@ -66,6 +66,8 @@ constexpr int kTileThreads = 256;       // 4 waves (one per SIMD)
 // about 1 % (T=4096: 0.660 -> 0.649 ms, T=16384: 2.425 -> 2.416 ms, same box), the
 // gate/up tiles, whose waves then read 43 % more from LDS per stage, lost 6 %.
 template <bool GATEUP> constexpr int big_waves() { return GATEUP ? 4 : 8; }
+// rounds of tiles per CU from which the 256-row down tiles run persistent workgroups
+constexpr int kPersistMinRounds = 24;
 constexpr int kXcds = 8;
 constexpr int kRowsPerLoad = 8;         // A rows one wave instruction moves
 constexpr int kFragBytes = 1024;        // one 16 x 32 bf16 MFMA fragment
@@ -736,7 +738,9 @@ __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d,
 // SPLIT (big shape only): every tile computes one slice of the contraction and
 // writes float32 partial sums (a separate instantiation, so that the plain big
 // kernels keep their registers).  The small shape handles both at run time.
-template <bool GATEUP, bool BIG, bool W8, bool SPLIT = false, bool WIDE = false>
+// PERSIST (big shape): the workgroups (one per CU) walk their XCD's share of the
+// list as the small shape's do, instead of one tile per workgroup.
+template <bool GATEUP, bool BIG, bool W8, bool SPLIT = false, bool WIDE = false, bool PERSIST = false>
 __global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
   typedef TileShape<GATEUP, BIG, W8, WIDE> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::kLdsBytes];
@@ -759,7 +763,7 @@ __global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) v
                                                  s_tile[3], s_tile[4],
                                                  decltype(list)::kSliced ? s_tile[5] : 0);
   };
-  if constexpr (BIG) {
+  if constexpr (BIG && !PERSIST) {
     // one tile per workgroup: the big shape's registers are nearly all taken by the
     // accumulators, and nothing may stay live across tiles
     if ((int)(blockIdx.x / kXcds) < list.entries()) run_tile(blockIdx.x / kXcds);
@@ -867,7 +871,8 @@ static long long tile_bound(const TileSeg& g, int kM) {
   return bound;
 }
 
-template <bool GATEUP, bool BIG, bool W8 = false, bool SPLIT = false, bool WIDE = false>
+template <bool GATEUP, bool BIG, bool W8 = false, bool SPLIT = false, bool WIDE = false,
+          bool PERSIST = false>
 static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStream_t st) {
   typedef TileShape<GATEUP, BIG, W8, WIDE> S;
   const TileSeg bb = b ? *b : TileSeg{};
@@ -878,7 +883,7 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
   const long long ba = tile_bound(a, S::kM) * nta, bbn = tile_bound(bb, S::kM) * ntb;
   long long per_xcd = (ba + kXcds - 1) / kXcds + (bbn + kXcds - 1) / kXcds;
   if (per_xcd == 0) return hipSuccess;
-  if (!BIG) {
+  if (!BIG || PERSIST) {
     // as many workgroups as fit the CUs at once (the LDS rings take most of a CU's
     // LDS), each walking its XCD's share of the list: the bound counts every
     // expert that could fall in the range, and a launch that finds none stays cheap
@@ -887,7 +892,7 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
   }
   const long long grid = per_xcd * kXcds;
   if (grid > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8, SPLIT, WIDE>), dim3((unsigned)grid), dim3(S::kThreads),
+  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8, SPLIT, WIDE, PERSIST>), dim3((unsigned)grid), dim3(S::kThreads),
                      0, st, a, bb, d);
   return hipGetLastError();
 }
@@ -948,7 +953,18 @@ hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const
   if (gateup)
     return wide ? launch_shape<true, false, false, false, true>(d, a, b, st)
                 : launch_shape<true, false>(d, a, b, st);
-  if (big) return launch_shape<false, true>(d, a, b, st);
+  if (big) {
+    // Persistent 256-row down tiles for a launch of many rounds (16384 tokens:
+    // 50 tiles per CU, down 2.46 -> 2.37 ms on one box); with few rounds (4096
+    // tokens: 12 per CU) one tile per workgroup is faster (0.66 against 0.69 ms):
+    // the hardware hands the next tile to whichever CU is free
+    typedef TileShape<false, true> S;
+    const long long tiles = tile_bound(a, S::kM) * (d / S::kWRows) +
+                            (b ? tile_bound(*b, S::kM) * (d / S::kWRows) : 0);
+    if (tiles >= (long long)kPersistMinRounds * device_cus())
+      return launch_shape<false, true, false, false, false, true>(d, a, b, st);
+    return launch_shape<false, true>(d, a, b, st);
+  }
   return wide ? launch_shape<false, false, false, false, true>(d, a, b, st)
               : launch_shape<false, false>(d, a, b, st);
 }
