@@ -257,7 +257,7 @@ Plan make_plan(const moge_dims_t* d) {
   const size_t part_bf16 = split_part_bytes(d, shared_split(d, false));
   const size_t part_w8 = d->dtype == MOGE_BF16 ? split_part_bytes(d, shared_split(d, true)) : 0;
   p.sh_part = take(part_bf16 > part_w8 ? part_bf16 : part_w8);
-  p.sched = take(moge::kSchedInts * 4);
+  p.sched = take(2 * moge::kSchedInts * 4);   // gate/up's counters, then down's
   p.total = o;
   return p;
 }
@@ -316,6 +316,8 @@ moge::TileSeg tile_view(const moge::FfnSeg& f, bool gateup) {
 // its range (an expert never has more rows than the batch has tokens).
 // split: contraction slices for the shared segment's 64-row tiles, with sh_part
 // the float32 partial-sum region (used when a slice count is above 1).
+// sched: 2 x kSchedInts ints, zero at the call, for the work counters of the
+// gate/up launch and then of the down launch; nullptr: launches that need none.
 moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh,
                       hipStream_t st, bool marks, SharedSplit split = SharedSplit{},
                       float* sh_part = nullptr, int* sched = nullptr) {
@@ -360,7 +362,8 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
       moge::TileSeg b = tile_view(*sh, gateup);
       b.thr = 0;
       b.thr_hi = INT_MAX;
-      CHECK(hip_check(moge::launch_ffn_mixed(gateup, d, a, b, gateup ? wide_gu : wide_dn, sched, st),
+      CHECK(hip_check(moge::launch_ffn_mixed(gateup, d, a, b, gateup ? wide_gu : wide_dn,
+                                             sched + (gateup ? 0 : moge::kSchedInts), st),
                       gateup ? "expert gate/up tiles (routed and shared)"
                              : "expert down tiles (routed and shared)"));
       if (marks) mark(gateup ? 4 : 5, st);
@@ -393,6 +396,9 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
         if (routed_here) CHECK(hip_check(moge::launch_ffn_tile(gateup, true, d, a, nullptr, st), what));
         CHECK(hip_check(moge::launch_ffn_tile(gateup, true, d, b, nullptr, st), what));
       } else {
+        // a gate/up launch of many rounds of 256-row tiles keeps its rounds with
+        // these counters
+        if (rg.big && gateup) a.rounds = sched;
         CHECK(hip_check(moge::launch_ffn_tile(gateup, rg.big, d, a, sh_here ? &b : nullptr, st,
                                               gateup ? wide_gu : wide_dn),
                         what));
@@ -518,8 +524,9 @@ moge_status_t layer_impl(const moge_dims_t* dims, const void* x, const void* w_r
   // S1+S2 softmax and grouped top-K'
   int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, p.idx);
   float* gate = topk_gate_out ? topk_gate_out : at<float>(ws, p.gate);
+  // (the routing kernel also zeroes the expert launches' work counters)
   CHECK(hip_check(moge::launch_route(scores, ksplit, T, N, M, kp, bias, logits_out, nullptr, idx,
-                                     gate, st),
+                                     gate, st, at<int>(ws, p.sched), 2 * moge::kSchedInts),
                   "route"));
   mark(2, st);
   // S3 permutation (the FFN gathers its rows from x through sorted_pair)

@@ -11,10 +11,11 @@ namespace moge {
 // partial[ks][t][e] = sum over the ks-th contraction split of x[t,:] . w_r[e,:]
 hipError_t launch_router_scores(int dtype, const void* x, const void* w_router, int T, int d,
                                 int N, int ksplit, float* partial, hipStream_t st);
-// scores = sum_ks partial (+ bias); softmax over N; per-group top-K'.
+// scores = sum_ks partial (+ bias); softmax over N; per-group top-K'.  The launch
+// also zeroes n_zero ints at `zero` (the layer's expert work counters).
 hipError_t launch_route(const float* partial, int ksplit, int T, int N, int M, int kp,
                         const float* bias, float* logits_out, float* probs, int32_t* idx,
-                        float* gate, hipStream_t st);
+                        float* gate, hipStream_t st, int* zero = nullptr, int n_zero = 0);
 int router_ksplit(int dtype, int T, int d, int N);
 
 // ---- permutation (permute.hip) ---------------------------------------------
@@ -136,6 +137,11 @@ struct TileSeg {
   // with few rows each, read once per launch, so that they do not push the
   // activation rows every weight tile re-reads out of L2)
   bool nt_weights = false;
+  // 256-row gate/up tiles: kSchedInts ints of device memory for round counters
+  // (16 ints apart, one per XCD, zero at launch), with which a launch of many
+  // rounds runs persistent workgroups that start each round of tiles together;
+  // nullptr: one tile per workgroup
+  int* rounds = nullptr;
 };
 // big: 256-row tiles; otherwise 64-row tiles (wide: 96-feature gate/up tiles,
 // needing a width divisible by 96, or 256-column down tiles, needing d % 256 == 0)
@@ -143,8 +149,8 @@ hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const
                            hipStream_t st, bool wide = false);
 // one projection (gate/up or down) of the routed experts on 64-row tiles (narrow
 // or wide) and of one unsplit shared segment on 256-row tiles, in one launch;
-// sched: kSchedInts ints of device memory the launch zeroes and uses as the XCDs'
-// work counters
+// sched: kSchedInts ints of device memory, zero at launch, that the launch uses as
+// the XCDs' work counters
 constexpr int kSchedInts = 16 * 8;
 hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const TileSeg& big,
                             bool wide, int* sched, hipStream_t st);

@@ -245,9 +245,13 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ partial
                                                float* __restrict__ logits_out,
                                                float* __restrict__ probs,
                                                int32_t* __restrict__ idx,
-                                               float* __restrict__ gate) {
+                                               float* __restrict__ gate,
+                                               int* __restrict__ zero, int n_zero) {
   __shared__ float s_l[kRouteWaves][256];
   __shared__ float s_p[kRouteWaves][256];
+  // the layer's work counters for the expert launches that follow
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int t = blockIdx.x * kRouteWaves + w;
   const bool valid = t < T;
@@ -323,11 +327,12 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ partial
 
 hipError_t launch_route(const float* partial, int ksplit, int T, int N, int M, int kp,
                         const float* bias, float* logits_out, float* probs, int32_t* idx,
-                        float* gate, hipStream_t st) {
-  if (ksplit < 1 || ksplit > kMaxRouterSplit) return hipErrorInvalidValue;
+                        float* gate, hipStream_t st, int* zero, int n_zero) {
+  if (ksplit < 1 || ksplit > kMaxRouterSplit || n_zero < 0 || (n_zero > 0 && !zero))
+    return hipErrorInvalidValue;
   dim3 grid((T + kRouteWaves - 1) / kRouteWaves);
   hipLaunchKernelGGL(k_route, grid, dim3(64 * kRouteWaves), 0, st, partial, ksplit, T, N, M, kp,
-                     bias, logits_out, probs, idx, gate);
+                     bias, logits_out, probs, idx, gate, zero, n_zero);
   return hipGetLastError();
 }
 

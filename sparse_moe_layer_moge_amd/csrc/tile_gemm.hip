@@ -46,7 +46,8 @@
 // XCD takes a contiguous eighth of every segment's list, so neighbouring entries
 // (an expert's row tiles of one weight tile, then its next weight tiles) run at
 // the same time on one XCD and share its L2; the segment with the longer
-// contraction is scheduled first.
+// contraction is scheduled first.  A 256-row gate/up launch of many rounds runs
+// persistent workgroups that keep their XCD's rounds together (k_ffn_tile).
 #include <limits.h>
 
 #include <type_traits>
@@ -66,8 +67,11 @@ constexpr int kTileThreads = 256;       // 4 waves (one per SIMD)
 // about 1 % (T=4096: 0.660 -> 0.649 ms, T=16384: 2.425 -> 2.416 ms, same box), the
 // gate/up tiles, whose waves then read 43 % more from LDS per stage, lost 6 %.
 template <bool GATEUP> constexpr int big_waves() { return GATEUP ? 4 : 8; }
-// rounds of tiles per CU from which the 256-row down tiles run persistent workgroups
+// rounds of tiles per CU from which the 256-row tiles run persistent workgroups
 constexpr int kPersistMinRounds = 24;
+// polls of a round counter before a workgroup goes on regardless (each an L2 round
+// trip and a short sleep: about a tile's time in all)
+constexpr int kRoundSpin = 64;
 constexpr int kXcds = 8;
 constexpr int kRowsPerLoad = 8;         // A rows one wave instruction moves
 constexpr int kFragBytes = 1024;        // one 16 x 32 bf16 MFMA fragment
@@ -384,7 +388,7 @@ struct TileList {
 // One tile: load, multiply and write it (every wave of the workgroup).
 template <bool GATEUP, bool BIG, bool W8, bool SPLIT, bool WIDE, int WAVES = 0>
 __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d, int e, int row0,
-                                             int rows, int nt, int kslice) {
+                                             int rows, int nt, int kslice, int* arrive = nullptr) {
   typedef bf16 E;
   typedef TileShape<GATEUP, BIG, W8, WIDE, WAVES> S;
   constexpr bool kSliced = !BIG || SPLIT;
@@ -634,6 +638,10 @@ __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d,
     main_loop(std::false_type{});
   else
     main_loop(std::true_type{});
+  // the round counter learns of this tile once its operands are read; the
+  // epilogue then runs while the rest of the round finishes
+  if (arrive && threadIdx.x == 0)
+    __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- epilogue ----------------------------------------------------------------
   // acc[q][p]: lane l, register r holds weight row 8*(r/4) + 4*(l/32) + r%4 of
@@ -754,34 +762,53 @@ __global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) v
   // (launched with as many workgroups as fit the CUs) walks on to b / 8 + G, b / 8 + 2G,
   // ... (G workgroups per XCD), so the CUs of an XCD work on neighbouring entries
   const int x = blockIdx.x % kXcds;
-  auto run_tile = [&](int it) {
+  auto run_tile = [&](int it, int* arrive) {
     if ((threadIdx.x >> 6) == 0) list.select(a, b, it, x, s_tile);
     __syncthreads();
     const int seg = s_tile[0];
     if (seg >= 0)
       tile_compute<GATEUP, BIG, W8, SPLIT, WIDE>(lds, seg == 0 ? a : b, d, s_tile[1], s_tile[2],
                                                  s_tile[3], s_tile[4],
-                                                 decltype(list)::kSliced ? s_tile[5] : 0);
+                                                 decltype(list)::kSliced ? s_tile[5] : 0, arrive);
+    else if (arrive && threadIdx.x == 0)
+      __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   if constexpr (BIG && !PERSIST) {
     // one tile per workgroup: the big shape's registers are nearly all taken by the
     // accumulators, and nothing may stay live across tiles
-    if ((int)(blockIdx.x / kXcds) < list.entries()) run_tile(blockIdx.x / kXcds);
+    if ((int)(blockIdx.x / kXcds) < list.entries()) run_tile(blockIdx.x / kXcds, nullptr);
   } else {
     const int gx = gridDim.x / kXcds;
-    for (int it = blockIdx.x / kXcds; it < list.entries(); it += gx) {
-      run_tile(it);
+    // Rounds (256-row tiles): the tiles of one round of an XCD's workgroups share a
+    // few activation row tiles and weight tiles, which stay in the XCD's L2 only
+    // while the tiles run side by side.  Left alone, the workgroups drift apart
+    // over a launch of many rounds; so each one, after its tile's epilogue, waits
+    // until every tile of its round has read its operands.  The wait is bounded
+    // (only L2 reuse rides on it; a workgroup that never arrives costs about a
+    // tile's time per round).  Skewed batch of 16384 tokens: L2 hit rate of the
+    // gate/up launch 0.58 -> 0.76, reads beyond L2 20.8 -> 11.7 GB, layer 7.14 ->
+    // 7.07 ms on one box.  A full barrier (waiting before the epilogue) gave the
+    // same hit rate but no time; the 256-row down tiles lost time with rounds.
+    int* const rounds = (BIG && PERSIST && a.rounds) ? a.rounds + 16 * x : nullptr;
+    int round = 0;
+    for (int it = blockIdx.x / kXcds; it < list.entries(); it += gx, ++round) {
+      run_tile(it, rounds);
       // every wave is done with this tile's LDS (and the descriptor) before the next
       __syncthreads();
+      if (rounds) {
+        if (threadIdx.x == 0) {
+          const int target = min(gx * (round + 1), list.entries());
+          for (int i = 0; i < kRoundSpin &&
+                          __hip_atomic_load(rounds, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target;
+               ++i)
+            __builtin_amdgcn_s_sleep(2);
+        }
+        __syncthreads();
+      }
     }
   }
 }
 
-
-__global__ void k_zero_i32(int* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
 
 // Both projections of a decode batch of a few hundred tokens: the routed experts
 // (a few dozen rows each) on 64-row tiles and the shared segment (every token) on
@@ -915,7 +942,6 @@ hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const Tile
               (tile_bound(small, 64) * (d / cs) + kXcds - 1) / kXcds;
   }
   if (per_xcd == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(kSchedInts), 0, st, sched, kSchedInts);
   const long long slots = device_cus() / kXcds;
   const long long grid = (per_xcd < slots ? per_xcd : (slots > 0 ? slots : 1)) * kXcds;
   const dim3 g((unsigned)grid), b(kTileThreads);
@@ -949,7 +975,15 @@ hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const
     return gateup ? launch_shape<true, true, false, true>(d, a, b, st)
                   : launch_shape<false, true, false, true>(d, a, b, st);
   }
-  if (gateup && big) return launch_shape<true, true>(d, a, b, st);
+  if (gateup && big) {
+    // persistent workgroups in rounds for a launch of many rounds
+    typedef TileShape<true, true> S;
+    const long long tiles = tile_bound(a, S::kM) * (a.inter / S::kFeat) +
+                            (b ? tile_bound(*b, S::kM) * (b->inter / S::kFeat) : 0);
+    if (a.rounds && tiles >= (long long)kPersistMinRounds * device_cus())
+      return launch_shape<true, true, false, false, false, true>(d, a, b, st);
+    return launch_shape<true, true>(d, a, b, st);
+  }
   if (gateup)
     return wide ? launch_shape<true, false, false, false, true>(d, a, b, st)
                 : launch_shape<true, false>(d, a, b, st);
@@ -961,9 +995,12 @@ hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const
     typedef TileShape<false, true> S;
     const long long tiles = tile_bound(a, S::kM) * (d / S::kWRows) +
                             (b ? tile_bound(*b, S::kM) * (d / S::kWRows) : 0);
+    // (without rounds: with them the down tiles measured slower, 2.30 -> 2.39 ms)
+    TileSeg a1 = a;
+    a1.rounds = nullptr;
     if (tiles >= (long long)kPersistMinRounds * device_cus())
-      return launch_shape<false, true, false, false, false, true>(d, a, b, st);
-    return launch_shape<false, true>(d, a, b, st);
+      return launch_shape<false, true, false, false, false, true>(d, a1, b, st);
+    return launch_shape<false, true>(d, a1, b, st);
   }
   return wide ? launch_shape<false, false, false, false, true>(d, a, b, st)
               : launch_shape<false, false>(d, a, b, st);
