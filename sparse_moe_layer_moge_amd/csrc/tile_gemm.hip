@@ -188,6 +188,18 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 
 typedef __attribute__((address_space(3))) void* LdsPtr;
 
+// f(std::integral_constant<int, n>) for a wave-uniform 0 <= n <= N
+template <int N, class F> __device__ __forceinline__ void with_count(int n, F&& f) {
+  if constexpr (N == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (n >= N)
+      f(std::integral_constant<int, N>{});
+    else
+      with_count<N - 1>(n, f);
+  }
+}
+
 // position of 16-byte chunk c of stage row r
 __device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
 
@@ -509,12 +521,12 @@ __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d,
   constexpr int kTP = S::kTP, kWP = S::kWP;
   constexpr int kSub = kTileK / 16;                  // MFMA sub-steps per stage
   const int wm = w % S::kWavesM, wn = w / S::kWavesM;
-  // 32-row blocks of this wave that hold rows of the tile.  A wave with fewer
-  // than kTP runs a second copy of the main loop that skips the MFMAs of the
-  // others (their loads still go out, in bounds, so that the wait counts stay
-  // the same): the last, nearly empty row tile of an expert then costs little
-  // more than streaming its weights once.  The full tiles keep a loop without
-  // the branches, which would otherwise cost them 5-7 %.
+  // 32-row blocks of this wave that hold rows of the tile.  The main loop has a
+  // copy for every count, which leaves out the MFMAs of the empty blocks (their
+  // loads still go out, in bounds, so that the wait counts stay the same): the
+  // last, nearly empty row tile of an expert then costs little more than
+  // streaming its weights once.  (A branch around each MFMA instead cost full
+  // tiles 5-7 %, and made partial 256-row tiles slower than full ones.)
   const int nact = __builtin_amdgcn_readfirstlane(max(0, min(kTP, (rows - wm * kTP * 32 + 31) >> 5)));
   f32x16 acc[kWP][kTP];
 #pragma unroll
@@ -553,8 +565,8 @@ __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d,
   // MFMAs of stage kb.  In between go out (one after every kEvery MFMAs, A first)
   // the A loads of stage kb + kDA - 1 when `next_a`, and the B loads of stage
   // kb + kDB - 1 when `next_b`.  Operand fragments are read one sub-step ahead.
-  // With `check`, the MFMAs of the wave's row blocks from nact on are skipped.
-  auto compute = [&](int kb, auto next_a, auto next_b, auto check) {
+  // Only the MFMAs of the wave's first `act` row blocks (a compile-time count).
+  auto compute = [&](int kb, auto next_a, auto next_b, auto act) {
     constexpr int na = decltype(next_a)::value ? S::kALoads : 0;
     constexpr int nl = na + (decltype(next_b)::value ? S::kBLoads : 0);
     const char* A = ldsA + (kb % S::kDA) * S::kAStageBytes;
@@ -568,7 +580,7 @@ __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d,
       for (int p = 0; p < kTP; ++p)
 #pragma unroll
         for (int q = 0; q < kWP; ++q) {
-          if (!decltype(check)::value || p < nact)
+          if (p < decltype(act)::value)
             acc[q][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[h & 1][q], tf[h & 1][p], acc[q][p], 0, 0, 0);
           const int m = (h * kTP + p) * kWP + q;
           const int j = m / S::kEvery;
@@ -611,7 +623,7 @@ __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d,
       for (int i = 0; i < S::kBLoads; ++i) issue_b(i, s);
     }
   }
-  auto main_loop = [&](auto check) {
+  auto main_loop = [&](auto act) {
   int kb = 0;
   // both operands of a later stage go out
   for (; kb + S::kDB - 1 < nk; ++kb) {
@@ -619,25 +631,22 @@ __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d,
     // every wave's loads of stage kb are in, and every wave has finished reading
     // the buffers the loads issued during this stage overwrite (stage kb - 1's)
     barrier_only();
-    compute(kb, std::true_type{}, std::true_type{}, check);
+    compute(kb, std::true_type{}, std::true_type{}, act);
   }
   // only activations of a later stage go out
   for (; kb + S::kDA - 1 < nk; ++kb) {
     wait_vmcnt_le<kPendSteady>(pending(kb));
     barrier_only();
-    compute(kb, std::true_type{}, std::false_type{}, check);
+    compute(kb, std::true_type{}, std::false_type{}, act);
   }
   // nothing goes out
   for (; kb < nk; ++kb) {
     wait_vmcnt_le<kPendSteady>(pending(kb));
     barrier_only();
-    compute(kb, std::false_type{}, std::false_type{}, check);
+    compute(kb, std::false_type{}, std::false_type{}, act);
   }
   };
-  if (nact == kTP)
-    main_loop(std::false_type{});
-  else
-    main_loop(std::true_type{});
+  with_count<kTP>(nact, main_loop);
   // the round counter learns of this tile once its operands are read; the
   // epilogue then runs while the rest of the round finishes
   if (arrive && threadIdx.x == 0)
