@@ -747,10 +747,13 @@ __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d,
   for (int i = tid; i < rows * kNC; i += S::kThreads) {
     const int r = i / kNC, c = i - r * kNC;
     const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * kPitch + ((c ^ (r & (kNCp - 1))) << 4));
-    // the 256-row tiles' outputs (H, y_perm) are read back by a later launch, not
-    // by this one: non-temporal, so that they do not push this round's operands
-    // out of L2 (16384 tokens: layer 7.05 -> 7.00 ms, down 2.30 -> 2.27 ms)
-    if constexpr (BIG)
+    // Outputs read back by a later launch, not by this one, go out non-temporal,
+    // so that they do not push the launch's operands out of L2: the 256-row
+    // tiles' H and y_perm (16384 tokens: layer 7.05 -> 7.00 ms, down 2.30 -> 2.27
+    // ms) and the 64-row down tiles' y_perm (456 tokens: down 0.218 -> 0.204 ms).
+    // The 64-row gate/up tiles keep H cached: their down launch reads it next
+    // (non-temporal H cost that gate/up stage 1.4 %).
+    if constexpr (BIG || !GATEUP)
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * ld + col0 + c * 8));
     else
       *reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * ld + col0 + c * 8) = v;
