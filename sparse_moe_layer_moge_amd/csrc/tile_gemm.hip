@@ -35,8 +35,8 @@
 // both (wide: 5 for gate/up, 4 for down), enough bytes in flight to cover HBM
 // latency with one workgroup per CU (on int8 codes 4 of both, 3 for the wide down
 // tile, two workgroups per CU).  An expert's last row tile is mostly partial: a
-// wave whose 32-row blocks are not all filled runs a copy of the main loop that
-// skips the MFMAs of the empty ones.
+// wave whose 32-row blocks are not all filled runs the copy of the main loop for
+// its count of filled blocks, which leaves out the MFMAs of the empty ones.
 //
 // The tiles of a segment form one list: for every expert in the shape's row range
 // ceil(rows / tile rows) row tiles, each paired with every weight tile (and
