@@ -204,8 +204,12 @@ SharedSplit shared_split(const moge_dims_t* d, bool w8) {
   // (down) per tile, narrow or wide as the launch will be; 256-row tiles: 96
   // features or 256 columns
   const long long R = (long long)T * d->M * d->k_per_group;
-  // the bf16 layer's mixed launches run the shared segment unsplit
-  if (!w8 && mixed_regime(true, routed_ranges(R, d->N, true), T)) return s;
+  // the bf16 layer's mixed launches run the shared gate/up unsplit and the shared
+  // down on kMixedDownSlices slices
+  if (!w8 && mixed_regime(true, routed_ranges(R, d->N, true), T)) {
+    if ((Is / 64) % moge::kMixedDownSlices == 0) s.dn = moge::kMixedDownSlices;
+    return s;
+  }
   if (w8 || T <= moge::kSharedSmallGateUpRows)
     s.gu = moge::tile_ksplit(
         T, d->d, Is / moge::small_gateup_feats(!w8 && wide_gateup(R, d->N, d->inter, Is)), 64);
@@ -314,8 +318,8 @@ moge::TileSeg tile_view(const moge::FfnSeg& f, bool gateup) {
 // has its own limits (kSharedStreamMaxRows, kSharedSmallGateUpRows,
 // kSharedSmallDownRows).  A tile launch is made only when some expert can fall in
 // its range (an expert never has more rows than the batch has tokens).
-// split: contraction slices for the shared segment's 64-row tiles, with sh_part
-// the float32 partial-sum region (used when a slice count is above 1).
+// split: contraction slices for the shared segment's tiles, with sh_part the
+// float32 partial-sum region (used when a slice count is above 1).
 // sched: 2 x kSchedInts ints, zero at the call, for the work counters of the
 // gate/up launch and then of the down launch; nullptr: launches that need none.
 moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh,
@@ -342,8 +346,9 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
   struct Range { int lo, hi, sh_lo, sh_hi; bool big; };
   // a batch whose routed experts all take 64-row tiles (none streams, none takes
   // 256-row tiles) while the shared segment takes 256-row tiles in both
-  // projections: one launch per projection for both, with the shared
-  // contraction unsplit (the routed tiles fill the CUs beside it)
+  // projections: one launch per projection for both, with the shared gate/up
+  // contraction unsplit (the routed tiles fill the CUs beside it) and the shared
+  // down one in kMixedDownSlices slices
   const bool mixed = sched && mixed_regime(tiles_ok, rr, sh ? sh->rows : 0);
   for (int gateup = 1; gateup >= 0; --gateup) {
     const int sh_big = gateup ? moge::kSharedSmallGateUpRows : moge::kSharedSmallDownRows;
@@ -362,6 +367,10 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
       moge::TileSeg b = tile_view(*sh, gateup);
       b.thr = 0;
       b.thr_hi = INT_MAX;
+      if (!gateup && split.dn > 1 && sh_part) {
+        b.ksplit = split.dn;
+        b.part = sh_part;
+      }
       CHECK(hip_check(moge::launch_ffn_mixed(gateup, d, a, b, gateup ? wide_gu : wide_dn,
                                              sched + (gateup ? 0 : moge::kSchedInts), st),
                       gateup ? "expert gate/up tiles (routed and shared)"

@@ -152,8 +152,18 @@ hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const
 // sched: kSchedInts ints of device memory, zero at launch, that the launch uses as
 // the XCDs' work counters
 constexpr int kSchedInts = 16 * 8;
+// big.ksplit > 1 (down only, with big.part): the shared tiles compute slices of the
+// contraction and write float32 partial sums, as a sliced segment does
 hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const TileSeg& big,
                             bool wide, int* sched, hipStream_t st);
+// Slices of the shared down projection's contraction in a mixed launch: a shared
+// 256-row down tile runs the whole shared intermediate width (5376 for four
+// experts of 1344), several times as long as a routed 64-row tile.  Two slices,
+// whose float32 partial sums the combine adds, took a 456-token batch's down
+// stage from 0.203 to 0.192 ms; three and four slices took 0.202-0.205 ms.
+// Slicing the shared gate/up tiles as well (with a SwiGLU pass over the partial
+// sums) made that stage slower, 0.353 -> 0.384 ms.
+constexpr int kMixedDownSlices = 2;
 // shapes the tile kernels cover (96-feature gate/up tiles, 256-column down tiles)
 bool tile_path_ok(int d, int inter);
 // 64-row tiles on int8 codes (tiles from `thr` rows up), and the shapes they cover

@@ -839,8 +839,9 @@ __global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) v
 // entries of that XCD's list (shared tiles first) one at a time from a counter of
 // their own, so neighbouring entries still run side by side there.  `sched` holds
 // the 8 counters, 16 ints apart, zero at launch.  The shared tiles run 4 waves
-// here, as the routed ones do.
-template <bool GATEUP, bool WIDE>
+// here, as the routed ones do.  BSPLIT: the shared tiles compute slices of the
+// contraction and write float32 partial sums (big.ksplit, big.part).
+template <bool GATEUP, bool WIDE, bool BSPLIT = false>
 __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_mixed(TileSeg small, TileSeg big, int d,
                                                                int* sched) {
   typedef TileShape<GATEUP, false, false, WIDE> SS;
@@ -857,7 +858,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_mixed(TileSeg small, Ti
   const TileSeg none{};
   TileList<GATEUP, false, false, false, WIDE> ls;
   ls.init(small, none, d);
-  TileList<GATEUP, true, false, false, false, 4> lb;
+  TileList<GATEUP, true, false, BSPLIT, false, 4> lb;
   lb.init(big, none, d);
   const int x = blockIdx.x % kXcds;
   const int nb = lb.entries(), n = nb + ls.entries();
@@ -878,7 +879,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_mixed(TileSeg small, Ti
     const int* t = is_big ? s_big : s_small;
     if (t[0] >= 0) {
       if (is_big)
-        tile_compute<GATEUP, true, false, false, false, 4>(lds, big, d, t[1], t[2], t[3], t[4], 0);
+        tile_compute<GATEUP, true, false, BSPLIT, false, 4>(lds, big, d, t[1], t[2], t[3], t[4],
+                                                            BSPLIT ? t[5] : 0);
       else
         tile_compute<GATEUP, false, false, false, WIDE>(lds, small, d, t[1], t[2], t[3], t[4], t[5]);
     }
@@ -944,7 +946,10 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
 
 hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const TileSeg& big,
                             bool wide, int* sched, hipStream_t st) {
-  if (big.ksplit != 1 || small.ksplit != 1 || !sched) return hipErrorInvalidValue;
+  // contraction slices: the shared segment's down tiles only, whole stages per slice
+  const bool bsplit = big.ksplit > 1;
+  if (big.ksplit < 1 || big.ksplit > kMaxSlices || small.ksplit != 1 || !sched) return hipErrorInvalidValue;
+  if (bsplit && (gateup || !big.part || (big.inter / kTileK) % big.ksplit)) return hipErrorInvalidValue;
   long long per_xcd;
   if (gateup) {
     typedef TileShape<true, true, false, false, 4> SB;
@@ -956,7 +961,7 @@ hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const Tile
     typedef TileShape<false, true, false, false, 4> SB;
     const int cs = small_down_cols(wide);
     if (d % SB::kWRows || d % cs) return hipErrorInvalidValue;
-    per_xcd = (tile_bound(big, SB::kM) * (d / SB::kWRows) + kXcds - 1) / kXcds +
+    per_xcd = (tile_bound(big, SB::kM) * (d / SB::kWRows) * big.ksplit + kXcds - 1) / kXcds +
               (tile_bound(small, 64) * (d / cs) + kXcds - 1) / kXcds;
   }
   if (per_xcd == 0) return hipSuccess;
@@ -967,6 +972,10 @@ hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const Tile
     hipLaunchKernelGGL((k_ffn_mixed<true, true>), g, b, 0, st, small, big, d, sched);
   else if (gateup)
     hipLaunchKernelGGL((k_ffn_mixed<true, false>), g, b, 0, st, small, big, d, sched);
+  else if (bsplit && wide)
+    hipLaunchKernelGGL((k_ffn_mixed<false, true, true>), g, b, 0, st, small, big, d, sched);
+  else if (bsplit)
+    hipLaunchKernelGGL((k_ffn_mixed<false, false, true>), g, b, 0, st, small, big, d, sched);
   else if (wide)
     hipLaunchKernelGGL((k_ffn_mixed<false, true>), g, b, 0, st, small, big, d, sched);
   else

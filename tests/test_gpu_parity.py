@@ -569,11 +569,11 @@ def test_layer_one_expert_per_group_takes_everything(lib, name, T):
     assert normwise_rel_err(values(out["y"])[tok], ref["y"]) <= tolerance(cfg)
 
 
-# split_shared: the layer splits the shared experts' contraction (a 64-token batch);
-# at 456 tokens the shared segment runs unsplit beside the routed tiles, so the
-# layer equals the step path bit for bit there
+# split_shared: the layer splits the shared experts' contraction (a 64-token batch:
+# both projections; 456 tokens: the down projection, whose shared tiles run beside
+# the routed ones); elsewhere the layer equals the step path bit for bit
 @pytest.mark.parametrize("name,T,split_shared", [("C0", 64, False), ("C1", 64, True),
-                                                 ("C1", 17, False), ("C2", 456, False)])
+                                                 ("C1", 17, False), ("C2", 456, True)])
 def test_layer_deterministic_and_equal_to_step_path(lib, name, T, split_shared):
     import torch
     cfg = CONFIGS[name]
@@ -609,9 +609,10 @@ def test_layer_deterministic_and_equal_to_step_path(lib, name, T, split_shared):
     lib.combine(dims, y_perm, pr, gate, sh, y)
     torch.cuda.synchronize()
     if split_shared:
-        # the layer splits the shared experts' contraction over several 64-row tiles
-        # and adds the float32 partial sums without the step path's bf16 rounding of
-        # H_s and of the shared output: the results differ by those roundings
+        # the layer splits the shared experts' contraction over several tiles and
+        # adds the float32 partial sums without the step path's bf16 rounding of the
+        # shared output (and of H_s, where gate/up is split too): the results
+        # differ by those roundings
         err = normwise_rel_err(values(to_host(y)), values(a["y"]))
         assert 0 < err <= 2 * 2.0 ** -8, err
     else:
