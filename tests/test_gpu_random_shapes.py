@@ -61,12 +61,18 @@ CASES = list(range(64))
 # choice, which uses only the mean rows per expert R / N:
 #   mean 50 (T=400, N=64, K=8): no streaming launch, no 256-row launch, so the
 #     64-row tiles take experts of any size, from a few rows to several hundred;
+#     the shared segment runs beside them on 256-row tiles (one full, one partial),
+#     its down contraction whole (width 192: 3 stages) or in two slices (two
+#     experts of 384, width 768: 12 stages);
 #   mean 512 (T=2048, N=16, K=4): every routed expert on 256-row tiles, the
 #     least-chosen ones with far fewer than 128 rows.
 EDGE_CASES = {
     "mean50-skewed": replace(C0, name="mean50-skewed", T=400, d=256, N=64, M=8, kp=1, inter=192,
                              n_shared=1, shared_inter=192, dtype="bf16", router_std=1.0 / 16,
                              zipf_s=1.2, seed=7),
+    "mean50-sliced-shared": replace(C0, name="mean50-sliced-shared", T=400, d=256, N=64, M=8,
+                                    kp=1, inter=192, n_shared=2, shared_inter=384,
+                                    dtype="bf16", router_std=1.0 / 16, zipf_s=1.2, seed=9),
     "mean512-skewed": replace(C0, name="mean512-skewed", T=2048, d=256, N=16, M=4, kp=1,
                               inter=192, n_shared=1, shared_inter=192, dtype="bf16",
                               router_std=1.0 / 16, zipf_s=1.2, seed=8),
@@ -102,7 +108,7 @@ def test_row_range_edges(lib, name):
     counts = np.bincount(O.route(S.make_scores(cfg, T=cfg.T), cfg.M, cfg.kp)["idx"].ravel(),
                          minlength=cfg.N)
     # the shapes reach what they are for
-    if name == "mean50-skewed":
+    if name.startswith("mean50"):
         assert counts.max() > 128 and counts.min() <= 32, counts
     else:
         assert counts.min() < 128, counts
