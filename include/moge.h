@@ -228,7 +228,7 @@ moge_status_t moge_layer_forward_packed(const moge_dims_t* dims, const void* x,
  * every GPU that loads the library holds its own copy until the process ends.
  * Dims whose moge_workspace_size() exceeds it give MOGE_ERR_UNSUPPORTED; at the
  * Pangu-Pro shape (d 5120, 64 experts, K 8, width 1344, shared width 5376) that
- * allows up to 512 tokens.  Arguments and results are those of
+ * allows up to 645 tokens.  Arguments and results are those of
  * moge_layer_forward_packed, bit for bit.  The current device must be the
  * stream's device (MOGE_ERR_INVALID_ARG otherwise); the first call on a device
  * looks up the array's address there.  It never allocates or frees memory.

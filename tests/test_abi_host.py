@@ -40,6 +40,14 @@ def test_workspace_size():
     assert lib.moge_workspace_size(None) == 0
 
 
+def test_noalloc_scratch_covers_the_documented_batch():
+    # include/moge.h: at the Pangu-Pro shape the fixed scratch array of the
+    # allocation-free entry point holds the workspace of up to 645 tokens
+    assert moge.NOALLOC_SCRATCH_BYTES == 128 << 20
+    assert moge.workspace_size(dims(T=645)) <= moge.NOALLOC_SCRATCH_BYTES
+    assert moge.workspace_size(dims(T=646)) > moge.NOALLOC_SCRATCH_BYTES
+
+
 def route(d, logits=FAKE, probs=None, idx=FAKE, gate=FAKE):
     return lib.moge_route(ctypes.byref(d) if d is not None else None, logits, probs, idx, gate,
                           None)
