@@ -314,19 +314,25 @@ struct TileList {
     // segments of at most 64 experts: per-lane tables (one round of loads for
     // both); larger ones are scanned again for every tile
     lanes = a.n_exp <= 64 && b.n_exp <= 64;
+    // row tiles of each segment, in locals: a choice at run time between two
+    // members read back through the object would put the object in scratch memory
+    int m0 = 0, m1 = 0;
     if (lanes) {
-      if (a.n_exp) la = seg_lanes<S::kM>(a, &ma);
-      if (b.n_exp) lb = seg_lanes<S::kM>(b, &mb);
+      if (a.n_exp) la = seg_lanes<S::kM>(a, &m0);
+      if (b.n_exp) lb = seg_lanes<S::kM>(b, &m1);
     } else {
-      ma = a.n_exp ? seg_total_tiles<S::kM>(a) : 0;
-      mb = b.n_exp ? seg_total_tiles<S::kM>(b) : 0;
+      m0 = a.n_exp ? seg_total_tiles<S::kM>(a) : 0;
+      m1 = b.n_exp ? seg_total_tiles<S::kM>(b) : 0;
     }
+    ma = m0;
+    mb = m1;
     // every XCD takes an equal share of each segment; the segment with the longer
     // contraction (more work per tile) goes first, so its tiles do not pile up at
     // the end
     b_first = (GATEUP ? d : b.inter) > (GATEUP ? d : a.inter);
-    tot0 = b_first ? mb * ntb : ma * nta;
-    tot1 = b_first ? ma * nta : mb * ntb;
+    const int w0 = m0 * nta, w1 = m1 * ntb;
+    tot0 = b_first ? w1 : w0;
+    tot1 = b_first ? w0 : w1;
     ch0 = (tot0 + kXcds - 1) / kXcds;
     ch1 = (tot1 + kXcds - 1) / kXcds;
   }
@@ -855,6 +861,10 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_mixed(TileSeg small, Ti
   int* s_small = reinterpret_cast<int*>(lds + SS::kDA * SS::kAStageBytes + (SS::kDB - 1) * SS::kBStageBytes);
   int* s_big = reinterpret_cast<int*>(lds + SB::kDA * SB::kAStageBytes + (SB::kDB - 1) * SB::kBStageBytes);
   int* s_it = s_big + 8;
+  constexpr int kOffS = SS::kDA * SS::kAStageBytes + (SS::kDB - 1) * SS::kBStageBytes;
+  constexpr int kOffB = SB::kDA * SB::kAStageBytes + (SB::kDB - 1) * SB::kBStageBytes;
+  static_assert(kOffS + 6 * 4 <= kOffB + 8 * 4 || kOffB + 9 * 4 <= kOffS,
+                "the entry overlaps neither descriptor (6 ints each)");
   const TileSeg none{};
   TileList<GATEUP, false, false, false, WIDE> ls;
   ls.init(small, none, d);
