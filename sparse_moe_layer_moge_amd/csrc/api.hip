@@ -126,12 +126,16 @@ struct Plan {
   int ksplit;
 };
 
-// Contraction slices of the shared experts' 64-row tile launches (gate/up, down);
-// 1 = not split.  A single segment of a few dozen rows makes too few tiles to
-// cover the CUs, so its contraction is split and the float32 partial sums are
-// added afterwards (gate/up: by k_swiglu_parts, down: by the combine).
+// Contraction slices of the shared experts' tile launches (gate/up, down); 1 = not
+// split.  A single segment of a few dozen rows makes too few tiles to cover the
+// CUs, so its contraction is split and the float32 partial sums are added
+// afterwards (gate/up: by k_swiglu_parts, down: by the combine).  dn_parts: the
+// down projection writes float32 partial sums even as one slice (the mixed
+// launches' shared tiles always do).
 struct SharedSplit {
   int gu = 1, dn = 1;
+  bool dn_parts = false;
+  bool down_parts() const { return dn > 1 || dn_parts; }
 };
 
 bool tiles_ok_for(const moge_dims_t* d) {
@@ -205,9 +209,11 @@ SharedSplit shared_split(const moge_dims_t* d, bool w8) {
   // features or 256 columns
   const long long R = (long long)T * d->M * d->k_per_group;
   // the bf16 layer's mixed launches run the shared gate/up unsplit and the shared
-  // down on kMixedDownSlices slices
+  // down on kMixedDownSlices slices (one where they do not divide its stages),
+  // as float32 partial sums either way
   if (!w8 && mixed_regime(true, routed_ranges(R, d->N, true), T)) {
     if ((Is / 64) % moge::kMixedDownSlices == 0) s.dn = moge::kMixedDownSlices;
+    s.dn_parts = true;
     return s;
   }
   if (w8 || T <= moge::kSharedSmallGateUpRows)
@@ -226,7 +232,8 @@ SharedSplit shared_split(const moge_dims_t* d, bool w8) {
 size_t split_part_bytes(const moge_dims_t* d, const SharedSplit& ss) {
   size_t part = 0;
   if (ss.gu > 1) part = (size_t)2 * ss.gu * d->T * d->shared_inter * 4;
-  if (ss.dn > 1 && (size_t)ss.dn * d->T * d->d * 4 > part) part = (size_t)ss.dn * d->T * d->d * 4;
+  if (ss.down_parts() && (size_t)ss.dn * d->T * d->d * 4 > part)
+    part = (size_t)ss.dn * d->T * d->d * 4;
   return part;
 }
 
@@ -348,7 +355,7 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
   // 256-row tiles) while the shared segment takes 256-row tiles in both
   // projections: one launch per projection for both, with the shared gate/up
   // contraction unsplit (the routed tiles fill the CUs beside it) and the shared
-  // down one in kMixedDownSlices slices
+  // down one as float32 partial sums of kMixedDownSlices slices (or one)
   const bool mixed = sched && mixed_regime(tiles_ok, rr, sh ? sh->rows : 0);
   for (int gateup = 1; gateup >= 0; --gateup) {
     const int sh_big = gateup ? moge::kSharedSmallGateUpRows : moge::kSharedSmallDownRows;
@@ -367,7 +374,7 @@ moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSe
       moge::TileSeg b = tile_view(*sh, gateup);
       b.thr = 0;
       b.thr_hi = INT_MAX;
-      if (!gateup && split.dn > 1 && sh_part) {
+      if (!gateup && split.down_parts() && sh_part) {
         b.ksplit = split.dn;
         b.part = sh_part;
       }
@@ -595,7 +602,7 @@ moge_status_t layer_impl(const moge_dims_t* dims, const void* x, const void* w_r
                   sh_part, at<int>(ws, p.sched)));
   // S7 combine (the shared term as the slices' partial sums when its down
   // projection was split)
-  const bool dn_parts = shared && split.dn > 1;
+  const bool dn_parts = shared && split.down_parts();
   CHECK(hip_check(moge::launch_combine(dims->dtype, T, K, dims->d, routed.y, pair_row, gate,
                                        shared && !dn_parts ? sh.y : nullptr,
                                        dn_parts ? sh_part : nullptr, dn_parts ? split.dn : 0, y,

@@ -152,8 +152,8 @@ hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const
 // sched: kSchedInts ints of device memory, zero at launch, that the launch uses as
 // the XCDs' work counters
 constexpr int kSchedInts = 16 * 8;
-// big.ksplit > 1 (down only, with big.part): the shared tiles compute slices of the
-// contraction and write float32 partial sums, as a sliced segment does
+// down: the shared tiles write float32 partial sums of big.ksplit slices (one or
+// more) to big.part, as a sliced segment does; gate/up: big.ksplit == 1
 hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const TileSeg& big,
                             bool wide, int* sched, hipStream_t st);
 // Slices of the shared down projection's contraction in a mixed launch: a shared

@@ -845,11 +845,14 @@ __global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) v
 // entries of that XCD's list (shared tiles first) one at a time from a counter of
 // their own, so neighbouring entries still run side by side there.  `sched` holds
 // the 8 counters, 16 ints apart, zero at launch.  The shared tiles run 4 waves
-// here, as the routed ones do.  BSPLIT: the shared tiles compute slices of the
-// contraction and write float32 partial sums (big.ksplit, big.part).
-template <bool GATEUP, bool WIDE, bool BSPLIT = false>
+// here, as the routed ones do.  The shared down tiles compute big.ksplit slices
+// of the contraction (one or more) and write float32 partial sums to big.part:
+// staging their 256 x 256 output through LDS as well took all 512 registers and
+// spilled 96 more per lane.
+template <bool GATEUP, bool WIDE>
 __global__ __launch_bounds__(kTileThreads, 1) void k_ffn_mixed(TileSeg small, TileSeg big, int d,
                                                                int* sched) {
+  constexpr bool BSPLIT = !GATEUP;
   typedef TileShape<GATEUP, false, false, WIDE> SS;
   typedef TileShape<GATEUP, true, false, false, 4> SB;
   static_assert(SS::kThreads == kTileThreads && SB::kThreads == kTileThreads,
@@ -956,10 +959,12 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
 
 hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const TileSeg& big,
                             bool wide, int* sched, hipStream_t st) {
-  // contraction slices: the shared segment's down tiles only, whole stages per slice
-  const bool bsplit = big.ksplit > 1;
+  // the shared down tiles: float32 partial sums of big.ksplit slices of whole
+  // stages; the shared gate/up tiles: unsplit
   if (big.ksplit < 1 || big.ksplit > kMaxSlices || small.ksplit != 1 || !sched) return hipErrorInvalidValue;
-  if (bsplit && (gateup || !big.part || (big.inter / kTileK) % big.ksplit)) return hipErrorInvalidValue;
+  if (gateup ? big.ksplit != 1
+             : big.n_exp && (!big.part || (big.inter / kTileK) % big.ksplit))
+    return hipErrorInvalidValue;
   long long per_xcd;
   if (gateup) {
     typedef TileShape<true, true, false, false, 4> SB;
@@ -982,10 +987,6 @@ hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const Tile
     hipLaunchKernelGGL((k_ffn_mixed<true, true>), g, b, 0, st, small, big, d, sched);
   else if (gateup)
     hipLaunchKernelGGL((k_ffn_mixed<true, false>), g, b, 0, st, small, big, d, sched);
-  else if (bsplit && wide)
-    hipLaunchKernelGGL((k_ffn_mixed<false, true, true>), g, b, 0, st, small, big, d, sched);
-  else if (bsplit)
-    hipLaunchKernelGGL((k_ffn_mixed<false, false, true>), g, b, 0, st, small, big, d, sched);
   else if (wide)
     hipLaunchKernelGGL((k_ffn_mixed<false, true>), g, b, 0, st, small, big, d, sched);
   else
