@@ -442,11 +442,19 @@ __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d,
 #pragma unroll
     for (int i = 0; i < S::kALoads; ++i) a_src[i] = (int)((unsigned)pair[i] / div);
   }
+  // Lanes of stage rows past the tile's last row take an offset past the end of
+  // the activation buffer (under 4 GiB): the buffer's range check returns zeros
+  // for them without a memory access, where a copy of the last row would cross
+  // L2 and the load path for MFMA rows the epilogue drops.  Every load still goes
+  // out, so the wait counts stay as they are.
+  constexpr uint32_t kPastEnd = 0xFFFFFFF0u;
   uint32_t a_voff[S::kALoads];
 #pragma unroll
   for (int i = 0; i < S::kALoads; ++i) {
     const int r = (wu * S::kALoads + i) * kRowsPerLoad + lr;
-    a_voff[i] = (uint32_t)(((size_t)a_src[i] * K + kb0 * kTileK + swz_chunk(r, l & 7) * 8) * sizeof(E));
+    a_voff[i] = r < rows ? (uint32_t)(((size_t)a_src[i] * K + kb0 * kTileK + swz_chunk(r, l & 7) * 8) *
+                                      sizeof(E))
+                         : kPastEnd;
   }
   // ---- B: the stage's weight rows in MFMA fragment order: fragment f = 2 rb + kh
   // holds rows 16 rb .. +15 and elements 32 kh .. +31 of the stage, lane j of the
