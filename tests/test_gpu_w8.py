@@ -134,10 +134,13 @@ def test_w8_layer_small(lib, name, T):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("name,T", [("C1", 64), ("C1", 17), ("C2", 456), ("C3", 4096)])
+@pytest.mark.parametrize("name,T", [("C1", 64), ("C1", 17), ("C2", 456), ("C2", 129),
+                                    ("C2", 300), ("C3", 4096)])
 def test_w8_layer_decode_sizes(lib, name, T):
     # (the prefill batch too: every routed expert then takes about eight 64-row
-    # tiles on int8 codes, the last one partial)
+    # tiles on int8 codes, the last one partial.  129 and 300 tokens: the shared
+    # segment's 64-row int8 tiles with a partial last row tile, beside routed
+    # experts that stream or take 64-row tiles)
     cfg = CONFIGS[name]
     inp, dw = layer_inputs(cfg, T)
     scores = S.make_scores(cfg, T=T)
