@@ -326,7 +326,8 @@ moge::TileSeg tile_view(const moge::FfnSeg& f, bool gateup) {
 // kSharedSmallDownRows).  A tile launch is made only when some expert can fall in
 // its range (an expert never has more rows than the batch has tokens).
 // split: contraction slices for the shared segment's tiles, with sh_part the
-// float32 partial-sum region (used when a slice count is above 1).
+// float32 partial-sum region (used when a slice count is above 1, and by the
+// mixed launches' shared down tiles whatever their count).
 // sched: 2 x kSchedInts ints, zero at the call, for the work counters of the
 // gate/up launch and then of the down launch; nullptr: launches that need none.
 moge_status_t run_ffn(int dtype, int d, int T, moge::FfnSeg& routed, moge::FfnSeg* sh,
