@@ -6,11 +6,13 @@
 // a GEMV-like and a GEMM-like mode by workload; these are the GEMM-like modes.  A
 // workgroup computes one tile; there are two tile shapes, chosen per expert by its
 // row count:
-//   big   (above 128 rows): 256 rows x (96 gate/up features | 256 output columns);
-//         gate/up: 4 waves (one per SIMD), 2 (rows) x 2 (weight rows), each 128
+//   big   (above 128 rows): 256 rows x (192 gate/up features | 256 output columns);
+//         gate/up: 8 waves (two per SIMD), 2 (rows) x 4 (weight rows), each 128
 //         rows x 96 weight rows as 4 x 3 blocks of 32x32 float32 accumulators;
-//         down: 8 waves (two per SIMD), 2 x 4, each 128 rows x 64 columns as 4 x 2
-//         blocks.  This one is bound by the matrix cores.
+//         down: 8 waves, 2 x 4, each 128 rows x 64 columns as 4 x 2 blocks.  This
+//         one is bound by the matrix cores.  The launches that split the
+//         contraction or mix in 64-row tiles take a 96-feature gate/up tile on 4
+//         waves (one per SIMD, 2 x 2, each again 128 x 96).
 //   small (up to 128 rows): 64 rows x (64 gate/up features | 128 output columns);
 //         4 waves, all on the same 64 rows, each with its own 32 weight rows.
 //         Wide: 64 rows x (96 features, waves 2 (rows) x 2 (weight rows) | 256
@@ -30,10 +32,10 @@
 //     contiguous in the packed weight layout) per instruction.
 // The loads of later stages are spread between the MFMAs of the current one; a
 // stage boundary is a wait for the wave's own loads plus a workgroup barrier.  The
-// big tile keeps 2 activation and 4 (gate/up) or 3 (down) weight stages in LDS;
-// the small tile keeps 6 of
-// both (wide: 5 for gate/up, 4 for down), enough bytes in flight to cover HBM
-// latency with one workgroup per CU (on int8 codes 4 of both, 3 for the wide down
+// big tile keeps 2 activation and 4 (gate/up) or 3 (down) weight stages in LDS
+// (the 8-wave gate/up tile 2 of both, its stages being 32 + 48 KiB); the small
+// tile keeps 6 of both (wide: 5 for gate/up, 4 for down), enough bytes in flight
+// to cover HBM latency with one workgroup per CU (on int8 codes 4 of both, 3 for the wide down
 // tile, two workgroups per CU).  An expert's last row tile is mostly partial: a
 // wave whose 32-row blocks are not all filled runs the copy of the main loop for
 // its count of filled blocks, which leaves out the MFMAs of the empty ones.
@@ -62,10 +64,14 @@ namespace moge {
 constexpr int kTileK = 64;              // contraction elements per stage
 constexpr int kLineBytes = kTileK * 2;  // one operand row of a stage (bf16)
 constexpr int kTileThreads = 256;       // 4 waves (one per SIMD)
-// Waves of a 256-row tile: 4 for gate/up, 8 (two per SIMD) for down.  With two
-// waves per SIMD one wave's MFMAs run while the other waits; the down tiles gained
-// about 1 % (T=4096: 0.660 -> 0.649 ms, T=16384: 2.425 -> 2.416 ms, same box), the
-// gate/up tiles, whose waves then read 43 % more from LDS per stage, lost 6 %.
+// Waves of a 256-row tile unless the launch says otherwise: 4 for gate/up, 8 (two
+// per SIMD) for down.  With two waves per SIMD one wave's MFMAs run while the
+// other waits; the down tiles gained about 1 % (T=4096: 0.660 -> 0.649 ms,
+// T=16384: 2.425 -> 2.416 ms, same box).  A 96-feature gate/up tile on 8 waves of
+// 64 x 96 read 43 % more from LDS per stage and lost 6 %; the 8-wave gate/up tile
+// of the plain launches (TileShape::kXL) instead doubles the features, keeping
+// each wave's 128 x 96: 29 % fewer operand bytes into LDS per flop (16384 tokens:
+// gate/up 4.34 -> 4.07 ms, 4096 tokens: 1.215 -> 1.172 ms, same box).
 template <bool GATEUP> constexpr int big_waves() { return GATEUP ? 4 : 8; }
 // rounds of tiles per CU from which the 256-row tiles run persistent workgroups
 constexpr int kPersistMinRounds = 24;
@@ -91,14 +97,18 @@ constexpr int kSmallW8Depth = 4;
 // WAVES: 0 for the shape's own wave count, 4 to force one wave per SIMD (a big
 // tile in a launch whose other tiles run 4 waves)
 template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false, int WAVES = 0> struct TileShape {
+  // the big gate/up tile on 8 waves: 192 features (384 weight rows), each wave
+  // 128 rows x 96 weight rows as the 4-wave tile's waves, two waves per SIMD
+  static constexpr bool kXL = BIG && GATEUP && WAVES == 8;
   static constexpr int kM = BIG ? 256 : 64;                       // rows per tile
-  static constexpr int kWRows = (BIG || WIDE) ? (GATEUP ? 192 : 256) : 128;  // weight rows per tile
+  static constexpr int kWRows =
+      kXL ? 384 : (BIG || WIDE) ? (GATEUP ? 192 : 256) : 128;    // weight rows per tile
   static constexpr int kFeat = kWRows / 2;                         // gate/up features per tile
   static constexpr int kWaves = WAVES ? WAVES : (BIG ? big_waves<GATEUP>() : 4);
   static constexpr int kThreads = kWaves * 64;
   // waves along the rows
   static constexpr int kWavesM =
-      BIG ? (kWaves == 8 ? (GATEUP ? 4 : 2) : 2) : ((WIDE && GATEUP) ? 2 : 1);
+      BIG ? 2 : ((WIDE && GATEUP) ? 2 : 1);
   static constexpr int kWavesN = kWaves / kWavesM;
   static constexpr int kTP = kM / kWavesM / 32;                    // 32-row blocks per wave
   static constexpr int kBlocksPerTile = kWRows / 32;               // 32-row weight blocks
@@ -113,7 +123,7 @@ template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false, int WAVES =
   // (24 KiB against 32), so its weights run 3 stages ahead and fill the LDS; the
   // weights, not the activations, were the operand its MFMAs waited for
   static constexpr int kDA = BIG ? 2 : kSmallDepth;   // activation stages in LDS
-  static constexpr int kDB = BIG ? (GATEUP ? 4 : 3) : kSmallDepth;   // weight stages in LDS
+  static constexpr int kDB = BIG ? (GATEUP ? (kXL ? 2 : 4) : 3) : kSmallDepth;   // weight stages in LDS
   static constexpr int kAStageBytes = kM * kLineBytes;
   // B stage: bf16 weights, kWRows / 8 fragments of 1 KiB; int8 codes, kWRows / 16
   // code tiles of 1 KiB (16 rows x 64 codes)
@@ -122,8 +132,10 @@ template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false, int WAVES =
   // wave instructions per stage: A (8 rows each), B (one fragment each)
   static constexpr int kALoads = kM / kRowsPerLoad / kWaves;
   static constexpr int kBLoads = kBStageBytes / kFragBytes / kWaves;
-  // one load after every kEvery MFMAs
-  static constexpr int kEvery = BIG ? 3 : 1;
+  // one load after every kEvery MFMAs (the 8-wave gate/up tile, whose next stage
+  // has only the current one's MFMAs to arrive in, every second: 16384 tokens,
+  // gate/up 4.12 -> 4.09 ms against every third, 4.28 every MFMA, 4.40 every fourth)
+  static constexpr int kEvery = kXL ? 2 : BIG ? 3 : 1;
   static_assert(kALoads * kWaves * kRowsPerLoad == kM &&
                 kBLoads * kWaves * kFragBytes == kBStageBytes, "loads cover a stage");
   static_assert(kDA <= kDB && (kDA == kDB || (kDA == 2 && kDB >= 3)), "ring depths");
@@ -372,7 +384,9 @@ struct TileList {
           // tiles (skewed batch of 16384 tokens: gate/up 4.69 -> 4.66 ms with
           // groups of 8, down 2.49 -> 2.44 ms with groups of 4).  An expert with
           // at most kGroupM row tiles keeps the plain order.
-          constexpr int kGroupM = GATEUP ? 8 : 4;
+          // (the 8-wave gate/up tile: groups of 16; 16384 tokens, gate/up 4.09 ->
+          // 4.07 ms against 8, 4.20 with 4)
+          constexpr int kGroupM = GATEUP ? (S::kXL ? 16 : 8) : 4;
           const int span = kGroupM * ntg;
           const int grp = j / span, first_mt = grp * kGroupM;
           const int gs = min(nrt - first_mt, kGroupM);
@@ -585,17 +599,24 @@ __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d,
     constexpr int nl = na + (decltype(next_b)::value ? S::kBLoads : 0);
     const char* A = ldsA + (kb % S::kDA) * S::kAStageBytes;
     const char* B = ldsB + (kb % S::kDB) * S::kBStageBytes;
-    bf16x8 wf[2][kWP], tf[2][kTP];
-    read_frags(A, B, 0, wf[0], tf[0]);
+    // the 8-wave gate/up tile reads each sub-step's fragments just before its
+    // MFMAs (its registers hold no second set; the other wave on the SIMD runs
+    // meanwhile)
+    constexpr int kNB = S::kXL ? 1 : 2;
+    bf16x8 wf[kNB][kWP], tf[kNB][kTP];
+    if (kNB == 2) read_frags(A, B, 0, wf[0], tf[0]);
 #pragma unroll
     for (int h = 0; h < kSub; ++h) {
-      if (h + 1 < kSub) read_frags(A, B, h + 1, wf[(h + 1) & 1], tf[(h + 1) & 1]);
+      if (kNB == 1)
+        read_frags(A, B, h, wf[0], tf[0]);
+      else if (h + 1 < kSub)
+        read_frags(A, B, h + 1, wf[(h + 1) % kNB], tf[(h + 1) % kNB]);
 #pragma unroll
       for (int p = 0; p < kTP; ++p)
 #pragma unroll
         for (int q = 0; q < kWP; ++q) {
           if (p < decltype(act)::value)
-            acc[q][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[h & 1][q], tf[h & 1][p], acc[q][p], 0, 0, 0);
+            acc[q][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[h % kNB][q], tf[h % kNB][p], acc[q][p], 0, 0, 0);
           const int m = (h * kTP + p) * kWP + q;
           const int j = m / S::kEvery;
           if (m % S::kEvery == S::kEvery - 1 && j < nl) {
@@ -780,15 +801,16 @@ __device__ __forceinline__ void tile_compute(char* lds, const TileSeg& g, int d,
 // kernels keep their registers).  The small shape handles both at run time.
 // PERSIST (big shape): the workgroups (one per CU) walk their XCD's share of the
 // list as the small shape's do, instead of one tile per workgroup.
-template <bool GATEUP, bool BIG, bool W8, bool SPLIT = false, bool WIDE = false, bool PERSIST = false>
-__global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
-  typedef TileShape<GATEUP, BIG, W8, WIDE> S;
+template <bool GATEUP, bool BIG, bool W8, bool SPLIT = false, bool WIDE = false, bool PERSIST = false,
+          int WV = 0>
+__global__ __launch_bounds__(BIG ? (WV ? WV : big_waves<GATEUP>()) * 64 : kTileThreads, 1) void k_ffn_tile(TileSeg a, TileSeg b, int d) {
+  typedef TileShape<GATEUP, BIG, W8, WIDE, WV> S;
   __shared__ __attribute__((aligned(1024))) char lds[S::kLdsBytes];
   // the tile descriptor lives in the last weight buffer, which the loads issued
   // before the main loop leave alone and later loads overwrite only after the
   // main loop's first barrier
   int* s_tile = reinterpret_cast<int*>(lds + S::kDA * S::kAStageBytes + (S::kDB - 1) * S::kBStageBytes);
-  TileList<GATEUP, BIG, W8, SPLIT, WIDE> list;
+  TileList<GATEUP, BIG, W8, SPLIT, WIDE, WV> list;
   list.init(a, b, d);
   // workgroup b runs on XCD b % 8 and takes that XCD's entry b / 8; the small shape
   // (launched with as many workgroups as fit the CUs) walks on to b / 8 + G, b / 8 + 2G,
@@ -799,7 +821,7 @@ __global__ __launch_bounds__(BIG ? big_waves<GATEUP>() * 64 : kTileThreads, 1) v
     __syncthreads();
     const int seg = s_tile[0];
     if (seg >= 0)
-      tile_compute<GATEUP, BIG, W8, SPLIT, WIDE>(lds, seg == 0 ? a : b, d, s_tile[1], s_tile[2],
+      tile_compute<GATEUP, BIG, W8, SPLIT, WIDE, WV>(lds, seg == 0 ? a : b, d, s_tile[1], s_tile[2],
                                                  s_tile[3], s_tile[4],
                                                  decltype(list)::kSliced ? s_tile[5] : 0, arrive);
     else if (arrive && threadIdx.x == 0)
@@ -951,9 +973,9 @@ static long long tile_bound(const TileSeg& g, int kM) {
 }
 
 template <bool GATEUP, bool BIG, bool W8 = false, bool SPLIT = false, bool WIDE = false,
-          bool PERSIST = false>
+          bool PERSIST = false, int WV = 0>
 static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStream_t st) {
-  typedef TileShape<GATEUP, BIG, W8, WIDE> S;
+  typedef TileShape<GATEUP, BIG, W8, WIDE, WV> S;
   const TileSeg bb = b ? *b : TileSeg{};
   const long long wa = GATEUP ? S::kFeat : S::kWRows;
   const long long nta = (GATEUP ? a.inter / wa : d / wa) * ((!BIG || SPLIT) ? a.ksplit : 1);
@@ -971,7 +993,7 @@ static hipError_t launch_shape(int d, const TileSeg& a, const TileSeg* b, hipStr
   }
   const long long grid = per_xcd * kXcds;
   if (grid > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8, SPLIT, WIDE, PERSIST>), dim3((unsigned)grid), dim3(S::kThreads),
+  hipLaunchKernelGGL((k_ffn_tile<GATEUP, BIG, W8, SPLIT, WIDE, PERSIST, WV>), dim3((unsigned)grid), dim3(S::kThreads),
                      0, st, a, bb, d);
   return hipGetLastError();
 }
@@ -1033,13 +1055,17 @@ hipError_t launch_ffn_tile(bool gateup, bool big, int d, const TileSeg& a, const
                   : launch_shape<false, true, false, true>(d, a, b, st);
   }
   if (gateup && big) {
-    // persistent workgroups in rounds for a launch of many rounds
-    typedef TileShape<true, true> S;
-    const long long tiles = tile_bound(a, S::kM) * (a.inter / S::kFeat) +
-                            (b ? tile_bound(*b, S::kM) * (b->inter / S::kFeat) : 0);
+    // the 8-wave 192-feature tile: widths on the tile path are multiples of 64 and
+    // of 96 (tile_path_ok), so of 192
+    typedef TileShape<true, true, false, false, 8> S;
+    if (a.inter % S::kFeat || (b && b->n_exp && b->inter % S::kFeat)) return hipErrorInvalidValue;
+    // persistent workgroups in rounds for a launch of many rounds (counted in
+    // 96-feature tiles)
+    const long long tiles = 2 * (tile_bound(a, S::kM) * (a.inter / S::kFeat) +
+                                 (b ? tile_bound(*b, S::kM) * (b->inter / S::kFeat) : 0));
     if (a.rounds && tiles >= (long long)kPersistMinRounds * device_cus())
-      return launch_shape<true, true, false, false, false, true>(d, a, b, st);
-    return launch_shape<true, true>(d, a, b, st);
+      return launch_shape<true, true, false, false, false, true, 8>(d, a, b, st);
+    return launch_shape<true, true, false, false, false, false, 8>(d, a, b, st);
   }
   if (gateup)
     return wide ? launch_shape<true, false, false, false, true>(d, a, b, st)
