@@ -164,7 +164,7 @@ hipError_t launch_ffn_mixed(bool gateup, int d, const TileSeg& small, const Tile
 // Slicing the shared gate/up tiles as well (with a SwiGLU pass over the partial
 // sums) made that stage slower, 0.353 -> 0.384 ms.
 constexpr int kMixedDownSlices = 2;
-// shapes the tile kernels cover (96-feature gate/up tiles, 256-column down tiles)
+// shapes the tile kernels cover (96- and 192-feature gate/up tiles, 256-column down tiles)
 bool tile_path_ok(int d, int inter);
 // 64-row tiles on int8 codes (tiles from `thr` rows up), and the shapes they cover
 // (wide: 256-column down tiles; gate/up tiles are always narrow)

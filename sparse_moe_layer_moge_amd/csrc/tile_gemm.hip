@@ -952,8 +952,9 @@ int small_gateup_feats(bool wide) {
 }
 
 bool tile_path_ok(int d, int inter) {
-  // big tiles: 96-feature gate/up and 256-column down tiles; small tiles: 64 and
-  // 128 (implied); 64-element stages
+  // big tiles: 96-feature gate/up (split and mixed launches) and 256-column down
+  // tiles; small tiles: 64 and 128 (implied); 64-element stages.  A width that is
+  // a multiple of 64 and of 96 is one of 192, the 8-wave gate/up tile's features
   return d % TileShape<false, true>::kWRows == 0 && d % kTileK == 0 && inter % kTileK == 0 &&
          inter % TileShape<true, true>::kFeat == 0;
 }
