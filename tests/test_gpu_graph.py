@@ -4,12 +4,14 @@ The library never allocates, never synchronises and never reads device data on
 the host, so one layer call can be captured into a graph.  The graph is replayed
 several times with eager work and synchronisations between the replays, and every
 replay must give the eager call's output bit for bit.  Covered: the row-major,
-packed and int8-weight layers."""
+packed and int8-weight layers, and the packed layer at the prefill sizes (256-row
+tiles; at 16384 tokens the persistent gate/up tiles whose round counters the
+routing kernel of the same call zeroes)."""
 import numpy as np
 import pytest
 
 from synth import inputs as S
-from synth.configs import C0, C1, C2
+from synth.configs import C0, C1, C2, C3, C4
 from tests.gpu_util import dims_of, layer_inputs, say, to_host
 
 
@@ -65,6 +67,7 @@ def test_layer_graph_replays_equal_eager(lib, cfg, T):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("kind,cfg,T", [("packed", C1, 64), ("packed", C2, 456),
+                                        ("packed", C3, 4096), ("packed", C4, 16384),
                                         ("int8", C1, 64), ("int8", C2, 456)])
 def test_packed_and_int8_layer_graph_replays_equal_eager(lib, kind, cfg, T):
     import torch
