@@ -96,7 +96,8 @@ constexpr int kSmallW8Depth = 4;
 // 0.144 ms); a launch of one round (the split shared segment of a small batch)
 // keeps more, narrower tiles.
 // WAVES: 0 for the shape's own wave count, 4 to force one wave per SIMD (a big
-// tile in a launch whose other tiles run 4 waves)
+// tile in a launch whose other tiles run 4 waves), 8 for the big gate/up tile of
+// 192 features on two waves per SIMD (kXL)
 template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false, int WAVES = 0> struct TileShape {
   // the big gate/up tile on 8 waves: 192 features (384 weight rows), each wave
   // 128 rows x 96 weight rows as the 4-wave tile's waves, two waves per SIMD
@@ -120,9 +121,10 @@ template <bool GATEUP, bool BIG, bool W8 = false, bool WIDE = false, int WAVES =
   // two workgroups per CU), about the bytes in flight of the narrow rings
   static constexpr int kSmallDepth =
       W8 ? (WIDE ? 3 : kSmallW8Depth) : (WIDE ? (GATEUP ? 5 : 4) : 6);
-  // The big gate/up tile's weight stages are smaller than its activation stages
-  // (24 KiB against 32), so its weights run 3 stages ahead and fill the LDS; the
-  // weights, not the activations, were the operand its MFMAs waited for
+  // The 4-wave big gate/up tile's weight stages are smaller than its activation
+  // stages (24 KiB against 32), so its weights run 3 stages ahead and fill the
+  // LDS; the weights, not the activations, were the operand its MFMAs waited for.
+  // The 8-wave one's stages (32 + 48 KiB) fit 2 deep
   static constexpr int kDA = BIG ? 2 : kSmallDepth;   // activation stages in LDS
   static constexpr int kDB = BIG ? (GATEUP ? (kXL ? 2 : 4) : 3) : kSmallDepth;   // weight stages in LDS
   static constexpr int kAStageBytes = kM * kLineBytes;
